@@ -1,0 +1,299 @@
+"""Seeded synthetic inputs for the grouped NT GEMMs: random operands, per-expert row
+counts, FP8 quantization with fine-grained scales, K-grouped packing.
+
+This module produces inputs only. It holds none of the GEMM's arithmetic, and both the
+HIP path (through the tests and the benchmark) and the CPU oracle consume the bytes it
+makes. It uses torch for random numbers and elementwise work, on CPU for small cases and
+on the GPU for full-size workloads (the bytes, not the device, are what both sides see).
+
+Recipes, each from the DeepGEMM pages the workloads come from:
+
+* Per-channel 1x128 cast of the K-grouped repro (issue "Non-deterministic numerical
+  problem of k_grouped_fp8_gemm_nt_contiguous", section "repro script"): for each channel
+  and each group of 128 consecutive tokens, scale = amax / 448; a zero amax takes a
+  caller-chosen value (`sf_val`); scales are floored at 1e-30; codes are
+  x * (1 / scale) converted to E4M3 (round to nearest even). Codes are clamped to +-448
+  before conversion so an fp32 product that lands a hair above 448 cannot become NaN.
+* The same cast's k-major packing: expert e's tokens, transposed to [channels][k_e], laid
+  end to end.
+* 1x128 per-token-group activation scales and 128x128 block weight scales (the "1d2d"
+  FP8 masked path named in PR "Fix cross-expert output overwrites in SM90 masked GEMM",
+  and the "blockwise-FP8" MoE of the SM120 graph-replay issue), stored with rows
+  contiguous inside each K block.
+* Power-of-two (UE8M0) scales, "2^k" in the SM120 issue's environment section. The
+  rounding rule is not printed there; the reading taken is the smallest power of two not
+  below amax / 448 (so no code saturates), and 2^0 for a zero amax.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+FP8_MAX = 448.0
+GROUP = 128  # elements per scale along K (and rows per weight block)
+SENTINEL_BF16 = 0xDEAD  # bit pattern pre-filled into outputs to detect stray writes
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def randn(shape, seed: int, device="cpu", std: float = 1.0, gen=None) -> torch.Tensor:
+    """N(0, std^2) values rounded once to bf16."""
+    g = gen if gen is not None else _gen(seed, device)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return (x * std).to(torch.bfloat16)
+
+
+def poisson_counts(G: int, lam: float, cap: int, seed: int) -> np.ndarray:
+    """Per-expert row counts ~ Poisson(lam), clipped to [0, cap], int32."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return np.clip(rng.poisson(lam, size=G), 0, cap).astype(np.int32)
+
+
+# --------------------------------------------------------------------------- scales
+
+
+def _scale_from_amax(amax: torch.Tensor, sf_fmt: str, zero_sf: float = 1.0):
+    """amax (float32) -> (scale as float32 values, scale in storage format)."""
+    if sf_fmt == "f32":
+        sf = amax / FP8_MAX
+        sf = torch.where(sf == 0, torch.full_like(sf, zero_sf), sf).clamp_min(1e-30)
+        return sf, sf.contiguous()
+    if sf_fmt == "ue8m0":
+        ratio = amax / FP8_MAX
+        mant, exp = torch.frexp(ratio)  # ratio = mant * 2^exp, 0.5 <= mant < 1
+        e = torch.where(mant == 0.5, exp - 1, exp)  # ceil(log2(ratio))
+        e = torch.where(ratio == 0, torch.zeros_like(e), e)
+        code = (e + 127).clamp(0, 254)
+        sf = torch.ldexp(torch.ones_like(ratio), code - 127)
+        return sf, code.to(torch.uint8).contiguous()
+    raise ValueError(f"unknown scale format {sf_fmt!r}")
+
+
+def _to_e4m3(x: torch.Tensor) -> torch.Tensor:
+    return x.clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def quant_rows_1x128(x: torch.Tensor, sf_fmt: str = "f32"):
+    """Activation rows x[R, K] -> (codes uint8 [R, K], scales [K/128, R]).
+
+    One scale per row per 128-element K group; the scale tensor is stored with rows
+    contiguous inside each K group. K must be a multiple of 128.
+    """
+    R, K = x.shape
+    assert K % GROUP == 0, "FP8 activations need K % 128 == 0"
+    xv = x.float().view(R, K // GROUP, GROUP)
+    amax = xv.abs().amax(dim=2)  # [R, K/128]
+    sf, sf_store = _scale_from_amax(amax, sf_fmt)
+    codes = _to_e4m3(xv * (1.0 / sf).unsqueeze(2)).view(R, K)
+    return codes.contiguous(), sf_store.t().contiguous()
+
+
+def quant_weight_128x128(w: torch.Tensor, sf_fmt: str = "f32"):
+    """Weight w[N, K] -> (codes uint8 [N, K], scales [ceil(N/128), K/128])."""
+    N, K = w.shape
+    assert K % GROUP == 0, "FP8 weights need K % 128 == 0"
+    nb = (N + GROUP - 1) // GROUP
+    wp = torch.zeros((nb * GROUP, K), dtype=torch.float32, device=w.device)
+    wp[:N] = w.float()
+    wv = wp.view(nb, GROUP, K // GROUP, GROUP)
+    amax = wv.abs().amax(dim=(1, 3))  # [nb, K/128]
+    sf, sf_store = _scale_from_amax(amax, sf_fmt)
+    codes = _to_e4m3(wv * (1.0 / sf)[:, None, :, None]).view(nb * GROUP, K)[:N]
+    return codes.contiguous(), sf_store
+
+
+def quant_weight_channel(w: torch.Tensor, sf_fmt: str = "f32"):
+    """Weight w[N, K] with one scale per row and 128-K group -> (codes, scales [K/128, N])."""
+    codes, sf = quant_rows_1x128(w, sf_fmt)
+    return codes, sf
+
+
+def quant_tokens_per_channel(x: torch.Tensor, sf_val: float = 1.0):
+    """The K-grouped repro's cast: x[T, C] (tokens x channels) -> (codes [T, C],
+    scales float32 [T/128, C]); a channel whose 128-token group is all zero gets sf_val."""
+    T, C = x.shape
+    assert T % GROUP == 0
+    xv = x.float().view(T // GROUP, GROUP, C)
+    amax = xv.abs().amax(dim=1)  # [T/128, C]
+    sf = amax / FP8_MAX
+    sf = torch.where(sf == 0, torch.full_like(sf, sf_val), sf).clamp_min(1e-30)
+    codes = _to_e4m3(xv * (1.0 / sf).unsqueeze(1)).view(T, C)
+    return codes.contiguous(), sf.contiguous()
+
+
+def pack_kmajor(x: torch.Tensor, ks) -> torch.Tensor:
+    """Tokens-by-channels x[T, C] -> flat packed buffer: expert e's tokens transposed to
+    [C][k_e], experts laid end to end (offset C * sum of earlier k)."""
+    T, C = x.shape
+    out = torch.empty(T * C, dtype=x.dtype, device=x.device)
+    p = 0
+    for k in ks:
+        out[p * C:(p + k) * C] = x[p:p + k].t().reshape(-1)
+        p += k
+    return out
+
+
+# --------------------------------------------------------------------------- problems
+
+
+@dataclass
+class Problem:
+    """One grouped-GEMM call's inputs. Tensors live on `device`; codes are uint8 (FP8)
+    or bfloat16 (BF16); `meta` holds the host-side description of the draw."""
+
+    variant: str
+    dtype: str
+    G: int
+    N: int
+    K: int
+    A: torch.Tensor
+    B: torch.Tensor
+    SFA: torch.Tensor | None = None
+    SFB: torch.Tensor | None = None
+    sf_fmt: str = "f32"
+    sfb_gran: str = "block128"
+    cap: int = 0  # masked
+    M: int = 0  # contiguous / K-grouped
+    counts: torch.Tensor | None = None  # masked, int32 [G]
+    m_indices: torch.Tensor | None = None  # contiguous, int32 [M]
+    ks: torch.Tensor | None = None  # K-grouped, int32 [G]
+    K_total: int = 0
+    meta: dict = field(default_factory=dict)
+
+    def valid_flops(self) -> float:
+        """2 * (valid rows) * N * K summed over experts (the throughput numerator)."""
+        if self.variant == "masked":
+            c = np.clip(self.meta["counts"], 0, self.cap)
+            return float(2 * int(c.sum()) * self.N * self.K)
+        if self.variant == "contiguous":
+            return float(2 * int(self.meta["valid_rows"]) * self.N * self.K)
+        return float(2 * self.M * self.N * int(np.sum(self.meta["ks"])))
+
+
+def _weights(dtype, G, N, K, gen, device, sf_fmt, sfb_gran, std=1.0):
+    """Per-expert weights B[G, N, K] and their scales, generated expert by expert."""
+    if dtype == "bf16":
+        B = torch.empty((G, N, K), dtype=torch.bfloat16, device=device)
+        for g in range(G):
+            B[g] = randn((N, K), 0, device, std, gen=gen)
+        return B, None
+    B = torch.empty((G, N, K), dtype=torch.uint8, device=device)
+    nb = (N + GROUP - 1) // GROUP
+    if sfb_gran == "block128":
+        shape = (G, nb, K // GROUP)
+    else:
+        shape = (G, K // GROUP, N)
+    sf_dtype = torch.float32 if sf_fmt == "f32" else torch.uint8
+    SFB = torch.empty(shape, dtype=sf_dtype, device=device)
+    for g in range(G):
+        w = randn((N, K), 0, device, std, gen=gen)
+        if sfb_gran == "block128":
+            B[g], SFB[g] = quant_weight_128x128(w, sf_fmt)
+        else:
+            B[g], SFB[g] = quant_weight_channel(w, sf_fmt)
+    return B, SFB
+
+
+def make_masked(dtype: str, G: int, cap: int, N: int, K: int, counts, seed: int,
+                device="cpu", sf_fmt="f32", sfb_gran="block128", std_a=1.0,
+                std_b=1.0) -> Problem:
+    """Masked problem: A[G, cap, K] (all rows drawn, padding included), B[G, N, K]."""
+    counts = np.asarray(counts, dtype=np.int32)
+    gen = _gen(seed, device)
+    if dtype == "bf16":
+        A = randn((G, cap, K), 0, device, std_a, gen=gen)
+        SFA = None
+    else:
+        A = torch.empty((G, cap, K), dtype=torch.uint8, device=device)
+        sf_dtype = torch.float32 if sf_fmt == "f32" else torch.uint8
+        SFA = torch.empty((G, K // GROUP, cap), dtype=sf_dtype, device=device)
+        for g in range(G):
+            A[g], SFA[g] = quant_rows_1x128(randn((cap, K), 0, device, std_a, gen=gen), sf_fmt)
+    B, SFB = _weights(dtype, G, N, K, gen, device, sf_fmt, sfb_gran, std_b)
+    return Problem("masked", dtype, G, N, K, A, B, SFA, SFB, sf_fmt, sfb_gran, cap=cap,
+                   counts=torch.tensor(counts, dtype=torch.int32, device=device),
+                   meta={"counts": counts, "seed": seed})
+
+
+def contiguous_indices(seg_counts, align: int = GROUP, M_max: int | None = None):
+    """Row-to-expert index for concatenated expert segments, each padded with -1 to a
+    multiple of `align`; then -1 up to M_max rows. Returns (int32 array, valid rows)."""
+    parts = []
+    for g, c in enumerate(seg_counts):
+        c = int(c)
+        padded = (c + align - 1) // align * align
+        seg = np.full(padded, -1, dtype=np.int32)
+        seg[:c] = g
+        parts.append(seg)
+    idx = np.concatenate(parts) if parts else np.zeros(0, np.int32)
+    if M_max is not None:
+        assert idx.size <= M_max, "segments exceed the row budget"
+        idx = np.concatenate([idx, np.full(M_max - idx.size, -1, np.int32)])
+    return idx, int(np.sum(seg_counts))
+
+
+def make_contiguous(dtype: str, G: int, N: int, K: int, seg_counts, seed: int,
+                    device="cpu", sf_fmt="f32", sfb_gran="block128", M_max=None,
+                    align=GROUP, std_a=1.0, std_b=1.0) -> Problem:
+    """Contiguous problem: A[M, K] with per-expert segments padded to `align` rows."""
+    idx, valid_rows = contiguous_indices(seg_counts, align, M_max)
+    M = idx.size
+    gen = _gen(seed, device)
+    a = randn((M, K), 0, device, std_a, gen=gen)
+    if dtype == "bf16":
+        A, SFA = a, None
+    else:
+        A, SFA = quant_rows_1x128(a, sf_fmt)
+    B, SFB = _weights(dtype, G, N, K, gen, device, sf_fmt, sfb_gran, std_b)
+    return Problem("contiguous", dtype, G, N, K, A, B, SFA, SFB, sf_fmt, sfb_gran, M=M,
+                   m_indices=torch.tensor(idx, dtype=torch.int32, device=device),
+                   meta={"seg_counts": np.asarray(seg_counts, np.int64),
+                         "m_indices": idx, "valid_rows": valid_rows, "seed": seed})
+
+
+def make_kgrouped(dtype: str, ks, M: int, N: int, seed: int, device="cpu",
+                  std_a=1e-7, std_b=0.4, sf_val=1.0, zero_channel_k=128,
+                  K_total: int | None = None) -> Problem:
+    """K-grouped problem after the repro recipe: grad_y[T, M] ~ N(0,1)*std_a,
+    act[T, N] ~ N(0,1)*std_b, channel 0 of grad_y zeroed inside every expert that has
+    exactly `zero_channel_k` tokens; both cast per channel per 128 tokens and packed
+    k-major. A = packed grad_y (rows = M channels), B = packed act (rows = N channels)."""
+    ks = [int(k) for k in ks]
+    T = sum(ks)
+    K_total = T if K_total is None else K_total
+    gen = _gen(seed, device)
+    gy = randn((T, M), 0, device, std_a, gen=gen)
+    act = randn((T, N), 0, device, std_b, gen=gen)
+    p = 0
+    for k in ks:
+        if k == zero_channel_k:
+            gy[p:p + k, 0] = 0
+        p += k
+    pad = K_total - T
+    if dtype == "bf16":
+        A = pack_kmajor(gy, ks)
+        B = pack_kmajor(act, ks)
+        SFA = SFB = None
+    else:
+        qa, SFA = quant_tokens_per_channel(gy, sf_val)
+        qb, SFB = quant_tokens_per_channel(act, sf_val)
+        A = pack_kmajor(qa, ks)
+        B = pack_kmajor(qb, ks)
+        if pad:
+            SFA = torch.cat([SFA, torch.ones((pad // GROUP, M), device=device)])
+            SFB = torch.cat([SFB, torch.ones((pad // GROUP, N), device=device)])
+    if pad:
+        A = torch.cat([A, torch.zeros(pad * M, dtype=A.dtype, device=device)])
+        B = torch.cat([B, torch.zeros(pad * N, dtype=B.dtype, device=device)])
+    return Problem("kgrouped", dtype, len(ks), N, K_total, A, B, SFA, SFB, "f32",
+                   "channel", M=M, K_total=K_total,
+                   ks=torch.tensor(ks, dtype=torch.int32, device=device),
+                   meta={"ks": np.asarray(ks, np.int64), "seed": seed, "sf_val": sf_val,
+                         "grad_y": gy, "act": act})

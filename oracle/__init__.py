@@ -1,0 +1,37 @@
+"""CPU FP64 oracle for grouped NT GEMM (masked / contiguous / K-grouped, BF16 and FP8).
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the package smoke check and the benchmark's
+CPU-baseline leg may import or run anything in this directory. The product library
+(the HIP kernels behind the C ABI and their Python binding) never imports it, and the
+two share no code: the oracle has its own decoders, its own bf16 rounding and its own
+layout arithmetic, written from the format definitions and the pages' descriptions.
+
+Parity status of each function (what pins it lives in tests/test_oracle_*.py):
+  decode_e4m3fn, decode_bf16, decode_ue8m0, round_to_bf16  pinned (spec values, torch)
+  grouped_gemm_masked / _contiguous / _kgrouped               pinned (brute force with
+      exact rationals, integer-exact cases, one-hot weights, cross-variant identities,
+      the zero-channel exact zero, the printed reference norm of the K-grouped repro)
+  calc_diff                                                   pinned (closed forms)
+"""
+
+from .formats import (  # noqa: F401
+    E4M3_MAX,
+    decode_bf16,
+    decode_e4m3fn,
+    decode_scale,
+    decode_ue8m0,
+    round_to_bf16,
+)
+from .grouped_gemm import (  # noqa: F401
+    SCALE_K,
+    calc_diff,
+    contiguous_row_expert,
+    dequant_act_rows,
+    dequant_weight_rows,
+    gemm_nt_fp64,
+    grouped_gemm_contiguous,
+    grouped_gemm_kgrouped,
+    grouped_gemm_masked,
+    kgrouped_layout,
+    valid_counts,
+)
