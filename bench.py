@@ -1,0 +1,264 @@
+"""Benchmark of the grouped NT GEMM hot path on one MI355X.
+
+One step = one grouped-GEMM call over one batch of synthetic inputs already resident in
+HBM: the group scheduler, operand and scale staging, MFMA main loop, FP8 scale promotion
+and the row-masked epilogue all run inside it. The default workload is the K-grouped
+FP8 weight-gradient GEMM of the DeepGEMM issue "Non-deterministic numerical problem of
+k_grouped_fp8_gemm_nt_contiguous" (ks [256, 128, 128, 256], 2048 x 2048 channels,
+per-channel 1x128 FP32 scales, accumulating into an FP32 output as that issue's call
+does); --workload picks any other named workload.
+
+Timing: `--warmup` untimed steps, then exactly `--steps` steps captured into one
+hipGraph and replayed once between HIP events recorded on the launch stream, bracketed
+by device synchronization (the pages' method also times graph-captured calls). Outputs
+rotate over enough buffers that their footprint exceeds the 256 MB Infinity Cache, so
+each step streams its output from HBM.
+
+Prints one JSON line with the metric, the roofline of the kernel and the CPU oracle's
+throughput on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="kgrouped_fp8_wgrad")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="output buffers to rotate over (0: enough to exceed the MALL)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(p, opt) -> int:
+    """Bytes a perfect kernel must move per call: every operand byte that feeds a valid
+    output once, every scale once, valid output rows written once (read once more when
+    accumulating)."""
+    import numpy as np
+    esz = 1 if p.dtype == "fp8" else 2
+    sf = 4 if p.sf_fmt == "f32" else 1
+    if p.variant == "kgrouped":
+        T = int(np.sum(p.meta["ks"]))
+        b = (p.M + p.N) * T * esz
+        if p.dtype == "fp8":
+            b += (T // 128) * (p.M + p.N) * sf
+        out = p.G * p.M * p.N * 4
+        return b + out * (2 if opt.get("accumulate", True) else 1)
+    if p.variant == "masked":
+        c = np.clip(p.meta["counts"], 0, p.cap)
+        rows, experts = int(c.sum()), int((c > 0).sum())
+    else:
+        idx = p.meta["m_indices"]
+        rows = int((idx >= 0).sum())
+        experts = len(set(idx[idx >= 0].tolist()))
+    b = rows * p.K * esz + experts * p.N * p.K * esz + rows * p.N * 2
+    if p.dtype == "fp8":
+        kb = p.K // 128
+        b += rows * kb * sf
+        b += experts * (((p.N + 127) // 128) * kb if p.sfb_gran == "block128" else p.N * kb) * sf
+    return b
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the grouped GEMM shards by expert across GPUs with no exchange inside the "
+              "kernel; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_grouped_gemm_nt_amd as mgg
+    from moe_grouped_gemm_nt_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mgg.load_library()
+    p, opt = synth.make_workload(args.workload, dev)
+    flops = p.valid_flops()
+    abytes = algorithmic_bytes(p, opt)
+
+    # Output buffers, rotated so their footprint exceeds the Infinity Cache.
+    if p.variant == "kgrouped":
+        out_shape, out_dtype = (p.G, p.M, p.N), torch.float32
+    elif p.variant == "masked":
+        out_shape, out_dtype = (p.G, p.cap, p.N), torch.bfloat16
+    else:
+        out_shape, out_dtype = (p.M, p.N), torch.bfloat16
+    out_bytes = int(np.prod(out_shape)) * (4 if out_dtype == torch.float32 else 2)
+    nrot = args.rotate if args.rotate > 0 else max(1, min(8, -(-2 * MALL_BYTES // out_bytes)))
+    outs = [torch.zeros(out_shape, dtype=out_dtype, device=dev) for _ in range(nrot)]
+
+    def step(i):
+        D = outs[i % nrot]
+        if p.variant == "kgrouped":
+            mgg.grouped_gemm_kgrouped(p.A, p.B, D, p.ks, p.M, p.N, p.SFA, p.SFB,
+                                      opt.get("accumulate", True))
+        elif p.variant == "masked":
+            mgg.grouped_gemm_masked(p.A, p.B, D, p.counts, p.SFA, p.SFB, p.sfb_gran,
+                                    opt["expected_m"])
+        else:
+            mgg.grouped_gemm_contiguous(p.A, p.B, D, p.m_indices, p.SFA, p.SFB, p.sfb_gran,
+                                        opt["expected_m"])
+
+    stream = torch.cuda.Stream(dev)
+    stream.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+    torch.cuda.synchronize(dev)
+    print(f"[bench] {args.workload}: warmup {args.warmup} done; capturing {args.steps} steps",
+          file=sys.stderr, flush=True)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(args.steps):
+            step(i)
+    torch.cuda.synchronize(dev)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    wall0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        t0.record(stream)
+        graph.replay()
+        t1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall0
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    print(f"[bench] timed {args.steps} steps: {ms_total:.3f} ms on the stream, "
+          f"{wall * 1e3:.3f} ms wall", file=sys.stderr, flush=True)
+
+    ai = flops / abytes
+    ridge = MFMA_PEAK_TFLOPS[p.dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    gbs = abytes / (ms_step * 1e-3) / 1e9
+    if ai < ridge:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1),
+                "peak": MFMA_PEAK_TFLOPS[p.dtype], "unit": "TFLOP/s",
+                "frac": round(tflops / MFMA_PEAK_TFLOPS[p.dtype], 4)}
+    roof["traffic"] = None
+    roof["algorithmic_bytes_per_launch"] = abytes
+    roof["avg_launch_us"] = round(ms_step * 1e3, 3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(p, opt, flops, args.cpu_seconds)
+
+    cfg = {"workload": args.workload, "variant": p.variant, "dtype": p.dtype, "G": p.G,
+           "N": p.N, "K": p.K, "valid_gflop": round(flops / 1e9, 4),
+           "rotating_output_buffers": nrot, "timing": "one hipGraph of `steps` calls"}
+    if p.variant == "kgrouped":
+        cfg.update(M=p.M, ks=[int(k) for k in p.meta["ks"]],
+                   accumulate=bool(opt.get("accumulate", True)), scales="f32 per channel 1x128")
+    elif p.variant == "masked":
+        cfg.update(cap=p.cap, expected_m=opt["expected_m"],
+                   valid_rows=int(np.clip(p.meta["counts"], 0, p.cap).sum()))
+    else:
+        cfg.update(M=p.M, expected_m=opt["expected_m"], valid_rows=int(p.meta["valid_rows"]))
+    line = {
+        "metric": "grouped FP8/BF16 GEMM TFLOPS (valid rows) + % of gfx950 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "mfma_peak_frac": round(tflops / MFMA_PEAK_TFLOPS[p.dtype], 4),
+        "dtype": p.dtype,
+        "data": "synthetic",
+        "config": cfg,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(p, opt, flops, target_s):
+    """The oracle, as it stands, on the host cores: a bounded sample of the same workload
+    (whole experts, or a subset of experts for the large masked shapes)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+
+    def codes(t):
+        t = t.detach().cpu().contiguous()
+        import torch
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+    if p.variant == "kgrouped":
+        A, B = codes(p.A), codes(p.B)
+        SFA = None if p.SFA is None else codes(p.SFA)
+        SFB = None if p.SFB is None else codes(p.SFB)
+        ks = list(p.meta["ks"])
+        run = lambda: oracle.grouped_gemm_kgrouped(p.dtype, A, B, ks, p.M, p.N, p.K_total, SFA,
+                                                   SFB, "f32")
+        unit_flops = flops
+        sample = "the whole workload (all experts) per pass"
+    elif p.variant == "masked":
+        c = np.clip(p.meta["counts"], 0, p.cap)
+        gs = [g for g in range(p.G) if c[g] > 0][:2]
+        A = codes(p.A[gs[0]:gs[-1] + 1])
+        B = codes(p.B[gs[0]:gs[-1] + 1])
+        SFA = None if p.SFA is None else codes(p.SFA[gs[0]:gs[-1] + 1])
+        SFB = None if p.SFB is None else codes(p.SFB[gs[0]:gs[-1] + 1])
+        cc = c[gs[0]:gs[-1] + 1]
+        run = lambda: oracle.grouped_gemm_masked(p.dtype, A, B, cc, SFA, SFB, p.sfb_gran, p.sf_fmt)
+        unit_flops = float(2 * int(cc.sum()) * p.N * p.K)
+        sample = f"experts {gs[0]}..{gs[-1]} of {p.G} per pass"
+    else:
+        idx = p.meta["m_indices"]
+        rows = np.nonzero(idx >= 0)[0][:2048]
+        A = codes(p.A)[rows]
+        SFA = None if p.SFA is None else codes(p.SFA)[:, rows]
+        B = codes(p.B)
+        SFB = None if p.SFB is None else codes(p.SFB)
+        sub = idx[rows]
+        run = lambda: oracle.grouped_gemm_contiguous(p.dtype, A, B, sub, SFA, SFB, p.sfb_gran,
+                                                     p.sf_fmt)
+        unit_flops = float(2 * rows.size * p.N * p.K)
+        sample = f"the first {rows.size} valid rows per pass"
+    passes, t = 0, 0.0
+    t0 = time.perf_counter()
+    while True:
+        run()
+        passes += 1
+        t = time.perf_counter() - t0
+        if t >= target_s or passes >= 50:
+            break
+    return {"value": round(unit_flops * passes / t / 1e12, 6), "unit": "TFLOPS",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{sample}; {passes} passes in {t:.1f} s (FP64 numpy/BLAS)"}
+
+
+if __name__ == "__main__":
+    main()

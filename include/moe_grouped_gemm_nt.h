@@ -1,0 +1,151 @@
+/*
+ * moe_grouped_gemm_nt.h - C ABI of the MI355X (gfx950) grouped NT GEMM library for
+ * mixture-of-experts layers.
+ *
+ * Three grouped products, each in BF16 or in FP8 E4M3 with fine-grained scales and
+ * FP32 accumulation. "NT" means both operands are stored with K contiguous and the
+ * product is D = A * B^T per expert.
+ *
+ *   grouped_gemm_masked      per-expert capacity, device-side valid-row counts; only
+ *                            valid rows are written (DeepGEMM PR "Fix cross-expert
+ *                            output overwrites in SM90 masked GEMM", sections
+ *                            "Description" and "Reproduction and validation").
+ *   grouped_gemm_contiguous  expert row segments concatenated, a device-side expert
+ *                            index per row (DeepGEMM issue "SM120 m_grouped_fp8
+ *                            contiguous kernel: illegal memory access at CUDA graph
+ *                            replay", sections "Environment" and the analysis comment).
+ *   grouped_gemm_kgrouped    weight-gradient form, D_e (+)= A_e * B_e^T over expert e's
+ *                            token slice, with per-channel scales on both operands
+ *                            (DeepGEMM issue "Non-deterministic numerical problem of
+ *                            k_grouped_fp8_gemm_nt_contiguous", section "repro script").
+ *
+ * Common rules for every entry point:
+ *  - Every pointer is caller-owned device memory; the caller allocates every output.
+ *  - The call validates its host arguments first. On any violation it returns an error
+ *    code and enqueues nothing.
+ *  - Otherwise it enqueues kernels on `stream` and returns without synchronizing. It
+ *    never allocates, frees, copies to or from the host, or reads device memory on the
+ *    host, so it may be captured into a hipGraph. All routing (counts, row indices,
+ *    per-expert K) is read from device memory by the kernels at run time, so a graph
+ *    replay sees whatever values those buffers hold at replay time.
+ *  - Results are bitwise identical from call to call on the same inputs, independent
+ *    of `expected_m`, of other experts' counts and of launch shapes: each output
+ *    element is produced by one lane, in ascending K order, with no atomics.
+ *  - FP8 E4M3 is the OCP "E4M3FN" byte format (max 448, no infinities). Scales are
+ *    either float32 (MGG_SF_F32) or one unsigned byte u per scale meaning 2^(u-127)
+ *    (MGG_SF_UE8M0). A scale covers 128 consecutive K elements of one row (1x128) or
+ *    a 128x128 block of a weight matrix.
+ *  - Accumulation is FP32; BF16 outputs are rounded to nearest even.
+ *  - Inputs must not overlap outputs (except C == D in grouped_gemm_kgrouped).
+ *  - Calls on one stream are ordered; calls that run concurrently on different streams
+ *    must use disjoint outputs.
+ */
+#ifndef MOE_GROUPED_GEMM_NT_H
+#define MOE_GROUPED_GEMM_NT_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MGG_OK = 0,
+  MGG_EINVAL = 1,       /* a host argument is invalid; nothing enqueued */
+  MGG_EUNSUPPORTED = 2, /* valid but outside what this build implements; nothing enqueued */
+  MGG_EHIP = 3          /* the HIP runtime reported an error at launch */
+} mgg_status;
+
+typedef enum { MGG_BF16 = 0, MGG_FP8_E4M3 = 1 } mgg_dtype;
+typedef enum { MGG_SF_F32 = 0, MGG_SF_UE8M0 = 1 } mgg_sf_fmt;
+typedef enum {
+  MGG_SFB_BLOCK128 = 0, /* one weight scale per 128x128 block */
+  MGG_SFB_CHANNEL = 1   /* one weight scale per weight row and 128-K group */
+} mgg_sfb_gran;
+
+/*
+ * Masked M-grouped NT GEMM: for every expert g and valid row m < clamp(masked_m[g], 0,
+ * cap), D[g, m, n] = sum_k A[g, m, k] * B[g, n, k] (dequantized for FP8).
+ *
+ *   dt          MGG_BF16 or MGG_FP8_E4M3 (both operands).
+ *   G, cap      experts and rows per expert (capacity); 1 <= G <= 4096, cap >= 1.
+ *   N, K        N >= 1 with N % 8 == 0; K >= 1 with K % 8 == 0 (BF16), K % 128 == 0 (FP8).
+ *   A           [G][cap][K] elements (bf16 or e4m3 bytes); 16-byte aligned.
+ *   SFA         FP8 only (else NULL): activation scales [G][K/128][cap], one per row and
+ *               128-K group, rows contiguous within each group.
+ *   B           [G][N][K] elements; 16-byte aligned.
+ *   SFB         FP8 only: BLOCK128 -> [G][ceil(N/128)][K/128]; CHANNEL -> [G][K/128][N].
+ *   sf, gran    scale storage format and weight-scale granularity (ignored for BF16).
+ *   D           bf16 [G][cap][N]; 16-byte aligned. Only valid rows are written: padding
+ *               rows and every byte outside the valid rows keep their previous contents.
+ *   masked_m    device int32 [G]; values outside [0, cap] are clamped (never a fault).
+ *   expected_m  host hint of the typical valid rows per expert (<= 0: unknown). It picks
+ *               a tile shape and never changes the result.
+ */
+mgg_status grouped_gemm_masked(mgg_dtype dt, int G, int cap, int N, int K,
+                               const void* A, const void* SFA,
+                               const void* B, const void* SFB,
+                               mgg_sf_fmt sf, mgg_sfb_gran gran,
+                               void* D, const int32_t* masked_m, int expected_m,
+                               hipStream_t stream);
+
+/*
+ * Contiguous M-grouped NT GEMM: row r belongs to expert e = m_indices[r] when e lies in
+ * [0, G); then D[r, n] = sum_k A[r, k] * B[e, n, k]. Rows with any other index are
+ * padding and are not written.
+ *
+ *   M           total rows, M >= 1 and M <= 524288.
+ *   A           [M][K] elements; SFA (FP8) [K/128][M].
+ *   B, SFB      as in grouped_gemm_masked (per expert).
+ *   D           bf16 [M][N].
+ *   m_indices   device int32 [M]. Contract: every aligned block of 128 rows holds rows
+ *               of at most one expert, valid rows first (segments padded with -1 to
+ *               multiples of 128). The expert of a block is the index of its first row;
+ *               a block whose first index is outside [0, G) is padding, and a row whose
+ *               index differs from its block's expert is not written. Never a fault.
+ */
+mgg_status grouped_gemm_contiguous(mgg_dtype dt, int G, int M, int N, int K,
+                                   const void* A, const void* SFA,
+                                   const void* B, const void* SFB,
+                                   mgg_sf_fmt sf, mgg_sfb_gran gran,
+                                   void* D, const int32_t* m_indices, int expected_m,
+                                   hipStream_t stream);
+
+/*
+ * K-grouped NT GEMM (weight gradient): expert e owns k_e = ks[e] consecutive tokens
+ * starting at token p_e = sum_{j<e} max(ks[j], 0). Operand blocks are packed per
+ * expert, tokens contiguous:
+ *   A: expert e's [M][k_e] block starts at element M * p_e;
+ *   B: expert e's [N][k_e] block starts at element N * p_e.
+ * D[e, i, j] = (accumulate ? D[e, i, j] : 0) + sum_{t < k_e} A_e[i, t] * B_e[j, t].
+ *
+ *   K_total     size of the token axis of both buffers (elements per channel).
+ *   SFA, SFB    FP8 only: per-channel scales [K_total/128][M] and [K_total/128][N];
+ *               token t of expert e uses scale row (p_e + t) / 128.
+ *   D           fp32 [G][M][N], 16-byte aligned.
+ *   ks          device int32 [G]. Contract: k_e >= 0; k_e and p_e multiples of 128
+ *               (FP8) or of 8 (BF16); p_e + k_e <= K_total. An expert outside the
+ *               contract is skipped (its D_e is not written). k_e == 0 gives D_e = 0
+ *               (accumulate == 0) or leaves D_e unchanged (accumulate == 1).
+ *   accumulate  1: D += product (the caller's C aliases D); 0: D = product.
+ *   FP8 scales must be MGG_SF_F32 or MGG_SF_UE8M0 and are per channel on both operands.
+ */
+mgg_status grouped_gemm_kgrouped(mgg_dtype dt, int G, int M, int N, int K_total,
+                                 const void* A, const void* SFA,
+                                 const void* B, const void* SFB,
+                                 mgg_sf_fmt sf,
+                                 float* D, const int32_t* ks, int accumulate,
+                                 hipStream_t stream);
+
+/* Human-readable text for a status code (static storage). */
+const char* mgg_status_string(mgg_status s);
+
+/* Text of the most recent error on the calling thread ("" if none). */
+const char* mgg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_GROUPED_GEMM_NT_H */

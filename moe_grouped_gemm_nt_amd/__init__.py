@@ -1,0 +1,197 @@
+"""Grouped NT GEMM for mixture-of-experts layers on MI355X (gfx950).
+
+Thin Python binding of the C ABI in include/moe_grouped_gemm_nt.h. It only marshals
+arguments: it derives sizes from tensor shapes, passes raw device pointers and the
+current HIP stream, and raises on a non-OK status. All computation happens in the HIP
+kernels of libmoe_grouped_gemm_nt.so; there is no fallback of any kind, and calling an
+entry point without the built library raises.
+
+Entry points (same names as the C functions):
+    grouped_gemm_masked(A, B, D, masked_m, SFA=None, SFB=None, sfb_gran="block128",
+                        expected_m=0)
+    grouped_gemm_contiguous(A, B, D, m_indices, SFA=None, SFB=None, sfb_gran="block128",
+                            expected_m=0)
+    grouped_gemm_kgrouped(A, B, D, ks, M, N, SFA=None, SFB=None, accumulate=True)
+
+Element types: bfloat16 tensors select BF16; uint8 (or float8_e4m3fn) tensors select
+FP8 E4M3. Scale tensors: float32 selects FP32 scales, uint8 selects UE8M0 scales.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "grouped_gemm_masked",
+    "grouped_gemm_contiguous",
+    "grouped_gemm_kgrouped",
+    "library_path",
+    "load_library",
+    "MggError",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libmoe_grouped_gemm_nt.so"
+_lib = None
+
+MGG_BF16, MGG_FP8_E4M3 = 0, 1
+MGG_SF_F32, MGG_SF_UE8M0 = 0, 1
+MGG_SFB_BLOCK128, MGG_SFB_CHANNEL = 0, 1
+_GRAN = {"block128": MGG_SFB_BLOCK128, "channel": MGG_SFB_CHANNEL}
+
+
+class MggError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, _LIB_NAME)
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the built HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m moe_grouped_gemm_nt_amd.build` "
+            "(there is no non-HIP implementation)")
+    lib = ctypes.CDLL(path)
+    vp, i32, st = ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p
+    lib.grouped_gemm_masked.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, i32,
+                                        vp, vp, i32, st]
+    lib.grouped_gemm_contiguous.argtypes = list(lib.grouped_gemm_masked.argtypes)
+    lib.grouped_gemm_kgrouped.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, vp,
+                                          vp, i32, st]
+    for f in (lib.grouped_gemm_masked, lib.grouped_gemm_contiguous, lib.grouped_gemm_kgrouped):
+        f.restype = ctypes.c_int
+    lib.mgg_status_string.argtypes = [ctypes.c_int]
+    lib.mgg_status_string.restype = ctypes.c_char_p
+    lib.mgg_last_error.argtypes = []
+    lib.mgg_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        msg = lib.mgg_last_error().decode() or lib.mgg_status_string(status).decode()
+        raise MggError(status, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _elem_dtype(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return MGG_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return MGG_FP8_E4M3
+    raise TypeError(f"operands must be bfloat16 or FP8 bytes, got {t.dtype}")
+
+
+def _sf_fmt(sf) -> int:
+    import torch
+    if sf is None:
+        return MGG_SF_F32
+    if sf.dtype == torch.float32:
+        return MGG_SF_F32
+    if sf.dtype == torch.uint8:
+        return MGG_SF_UE8M0
+    raise TypeError(f"scales must be float32 or uint8 (UE8M0), got {sf.dtype}")
+
+
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    _require(len(devs) == 1 and next(iter(devs)).type == "cuda",
+             "all tensors must be on the same GPU")
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None:
+            _require(t.is_contiguous(), "tensors must be contiguous")
+
+
+def grouped_gemm_masked(A, B, D, masked_m, SFA=None, SFB=None, sfb_gran="block128",
+                        expected_m=0):
+    """D[g, m, :] = A[g, m, :] @ B[g].T for m < masked_m[g]; A[G, cap, K], B[G, N, K],
+    D bf16 [G, cap, N], masked_m int32 [G] on the device."""
+    import torch
+    lib = load_library()
+    _same_device(A, B, D, masked_m, SFA, SFB)
+    _contig(A, B, D, masked_m, SFA, SFB)
+    G, cap, K = A.shape
+    N = B.shape[1]
+    _require(tuple(B.shape) == (G, N, K), "B must be [G, N, K]")
+    _require(tuple(D.shape) == (G, cap, N) and D.dtype == torch.bfloat16, "D must be bf16 [G, cap, N]")
+    _require(masked_m.dtype == torch.int32 and masked_m.numel() == G, "masked_m must be int32 [G]")
+    dt = _elem_dtype(A)
+    _require(_elem_dtype(B) == dt, "A and B must have the same element type")
+    with torch.cuda.device(A.device):
+        _check(lib.grouped_gemm_masked(dt, G, cap, N, K, _ptr(A), _ptr(SFA), _ptr(B), _ptr(SFB),
+                                       _sf_fmt(SFA), _GRAN[sfb_gran], _ptr(D), _ptr(masked_m),
+                                       int(expected_m), _stream(A.device)))
+    return D
+
+
+def grouped_gemm_contiguous(A, B, D, m_indices, SFA=None, SFB=None, sfb_gran="block128",
+                            expected_m=0):
+    """D[r, :] = A[r, :] @ B[m_indices[r]].T for rows with a valid expert index;
+    A[M, K], B[G, N, K], D bf16 [M, N], m_indices int32 [M] on the device."""
+    import torch
+    lib = load_library()
+    _same_device(A, B, D, m_indices, SFA, SFB)
+    _contig(A, B, D, m_indices, SFA, SFB)
+    M, K = A.shape
+    G, N, _ = B.shape
+    _require(B.shape[2] == K, "B must be [G, N, K]")
+    _require(tuple(D.shape) == (M, N) and D.dtype == torch.bfloat16, "D must be bf16 [M, N]")
+    _require(m_indices.dtype == torch.int32 and m_indices.numel() == M, "m_indices must be int32 [M]")
+    dt = _elem_dtype(A)
+    _require(_elem_dtype(B) == dt, "A and B must have the same element type")
+    with torch.cuda.device(A.device):
+        _check(lib.grouped_gemm_contiguous(dt, G, M, N, K, _ptr(A), _ptr(SFA), _ptr(B), _ptr(SFB),
+                                           _sf_fmt(SFA), _GRAN[sfb_gran], _ptr(D),
+                                           _ptr(m_indices), int(expected_m), _stream(A.device)))
+    return D
+
+
+def grouped_gemm_kgrouped(A, B, D, ks, M, N, SFA=None, SFB=None, accumulate=True):
+    """D[e] (+)= A_e @ B_e.T over expert e's ks[e] tokens; A, B flat packed buffers
+    (expert blocks [M][k_e] / [N][k_e]), D fp32 [G, M, N], ks int32 [G] on the device."""
+    import torch
+    lib = load_library()
+    _same_device(A, B, D, ks, SFA, SFB)
+    _contig(A, B, D, ks, SFA, SFB)
+    G = ks.numel()
+    _require(A.numel() % M == 0 and B.numel() % N == 0, "packed buffers must hold whole channels")
+    K_total = A.numel() // M
+    _require(B.numel() // N == K_total, "A and B must cover the same token axis")
+    _require(tuple(D.shape) == (G, M, N) and D.dtype == torch.float32, "D must be fp32 [G, M, N]")
+    _require(ks.dtype == torch.int32, "ks must be int32")
+    dt = _elem_dtype(A)
+    _require(_elem_dtype(B) == dt, "A and B must have the same element type")
+    with torch.cuda.device(A.device):
+        _check(lib.grouped_gemm_kgrouped(dt, G, M, N, K_total, _ptr(A), _ptr(SFA), _ptr(B),
+                                         _ptr(SFB), _sf_fmt(SFA), _ptr(D), _ptr(ks),
+                                         1 if accumulate else 0, _stream(A.device)))
+    return D

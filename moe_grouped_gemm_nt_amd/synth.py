@@ -297,3 +297,68 @@ def make_kgrouped(dtype: str, ks, M: int, N: int, seed: int, device="cpu",
                    ks=torch.tensor(ks, dtype=torch.int32, device=device),
                    meta={"ks": np.asarray(ks, np.int64), "seed": seed, "sf_val": sf_val,
                          "grad_y": gy, "act": act})
+
+
+# --------------------------------------------------------------------------- workloads
+#
+# The grouped-GEMM shapes the DeepGEMM pages run or quote, with synthetic values:
+#   masked_bf16_repro      PR "Fix cross-expert output overwrites": its reproduction script
+#   kgrouped_fp8_wgrad     issue "Non-deterministic numerical problem of
+#                          k_grouped_fp8_gemm_nt_contiguous": its repro script
+#   masked_fp8_g32_n1536   PR's latency table, row G=32 cap=4096 N=1536 K=2048 expected M 20
+#   contig_fp8_w13/_w2     SM120 issue's environment: G=288, per-rank w13 N=512/K=4096 and
+#                          w2 N=4096/K=256, power-of-two scales, expected M per group 113
+#   masked_*_g32_n6144     PR's latency table, row G=32 cap=4096 N=6144 K=7168 expected M 192
+#   masked_*_g6_n4096      PR's latency table, row G=6 cap=4096 N=K=4096 expected M 1024
+# Per-expert valid rows are drawn ~Poisson(expected M), clipped to the capacity (the
+# pages give only the expected value; the distribution is this build's choice).
+
+WORKLOADS = {
+    "masked_bf16_repro": dict(variant="masked", dtype="bf16", G=8, cap=32, N=256, K=256,
+                              counts=[0, 1, 16, 31, 32, 1, 32, 32], expected_m=32, seed=29),
+    "kgrouped_fp8_wgrad": dict(variant="kgrouped", dtype="fp8", ks=[256, 128, 128, 256],
+                               M=2048, N=2048, seed=0, sf_val=1.0, accumulate=True),
+    "masked_fp8_g32_n1536": dict(variant="masked", dtype="fp8", G=32, cap=4096, N=1536,
+                                 K=2048, lam=20, expected_m=20, seed=1),
+    "contig_fp8_w13": dict(variant="contiguous", dtype="fp8", G=288, N=512, K=4096, lam=113,
+                           expected_m=113, seed=2, sf_fmt="ue8m0", rows_per_expert_max=256),
+    "contig_fp8_w2": dict(variant="contiguous", dtype="fp8", G=288, N=4096, K=256, lam=113,
+                          expected_m=113, seed=3, sf_fmt="ue8m0", rows_per_expert_max=256),
+    "masked_fp8_g32_n6144": dict(variant="masked", dtype="fp8", G=32, cap=4096, N=6144,
+                                 K=7168, lam=192, expected_m=192, seed=4),
+    "masked_bf16_g32_n6144": dict(variant="masked", dtype="bf16", G=32, cap=4096, N=6144,
+                                  K=7168, lam=192, expected_m=192, seed=4),
+    "masked_fp8_g6_n4096": dict(variant="masked", dtype="fp8", G=6, cap=4096, N=4096,
+                                K=4096, lam=1024, expected_m=1024, seed=5),
+    "masked_bf16_g6_n4096": dict(variant="masked", dtype="bf16", G=6, cap=4096, N=4096,
+                                 K=4096, lam=1024, expected_m=1024, seed=5),
+}
+
+
+def contiguous_draw(G: int, lam: float, seed: int, rows_max: int):
+    """Per-expert rows ~ Poisson(lam), at most rows_max - 127 so every padded segment fits
+    in rows_max rows (the fixed row budget M = G * rows_max)."""
+    return poisson_counts(G, lam, rows_max - GROUP + 1, seed)
+
+
+def make_workload(name: str, device="cuda", **override) -> tuple[Problem, dict]:
+    """Problem for a named workload plus the call options (expected_m, accumulate)."""
+    w = dict(WORKLOADS[name])
+    w.update(override)
+    v = w["variant"]
+    if v == "masked":
+        counts = w.get("counts")
+        if counts is None:
+            counts = poisson_counts(w["G"], w["lam"], w["cap"], w["seed"])
+        p = make_masked(w["dtype"], w["G"], w["cap"], w["N"], w["K"], counts, w["seed"], device,
+                        sf_fmt=w.get("sf_fmt", "f32"), sfb_gran=w.get("sfb_gran", "block128"))
+        return p, {"expected_m": w["expected_m"]}
+    if v == "contiguous":
+        segs = contiguous_draw(w["G"], w["lam"], w["seed"], w["rows_per_expert_max"])
+        p = make_contiguous(w["dtype"], w["G"], w["N"], w["K"], segs, w["seed"], device,
+                            sf_fmt=w.get("sf_fmt", "f32"), sfb_gran=w.get("sfb_gran", "block128"),
+                            M_max=w["G"] * w["rows_per_expert_max"])
+        return p, {"expected_m": w["expected_m"]}
+    p = make_kgrouped(w["dtype"], w["ks"], w["M"], w["N"], w["seed"], device,
+                      sf_val=w.get("sf_val", 1.0))
+    return p, {"accumulate": w.get("accumulate", True)}

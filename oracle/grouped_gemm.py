@@ -182,16 +182,16 @@ def grouped_gemm_contiguous(dtype, A, B, m_indices, SFA=None, SFB=None,
 def kgrouped_layout(ks, K_total: int, granule: int):
     """Per-expert (offset p_e, length k_e, usable) of the packed K-grouped operands.
 
-    p_e = sum_{j<e} max(ks[j], 0). An expert is usable when 0 <= k_e, k_e is a multiple
-    of `granule` (128 for FP8, so that every 128-token scale group lies inside one
-    expert; 8 for BF16) and p_e + k_e <= K_total. Unusable experts are out of contract
-    and have no defined output.
+    p_e = sum_{j<e} max(ks[j], 0). An expert is usable when 0 <= k_e, both k_e and p_e
+    are multiples of `granule` (128 for FP8, so that every 128-token scale group lies
+    inside one expert; 8 for BF16) and p_e + k_e <= K_total. Unusable experts are out of
+    contract and have no defined output.
     """
     ks = np.asarray(ks, dtype=np.int64)
     out = []
     p = 0
     for k in ks:
-        usable = bool(k >= 0 and k % granule == 0 and p + k <= K_total)
+        usable = bool(k >= 0 and k % granule == 0 and p % granule == 0 and p + k <= K_total)
         out.append((p, int(k), usable))
         p += max(int(k), 0)
     return out

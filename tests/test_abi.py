@@ -1,0 +1,141 @@
+"""The C-ABI library: it loads, exports every function include/*.h declares, and rejects
+invalid host arguments before touching the GPU (these calls enqueue nothing, so they
+run without a GPU). CPU only."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import moe_grouped_gemm_nt_amd as mgg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+EINVAL, EUNSUPPORTED = 1, 2
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                            text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mgg.library_path()):
+        pytest.fail("library not built: run `python -m moe_grouped_gemm_nt_amd.build`")
+    return mgg.load_library()
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for f in ("grouped_gemm_masked", "grouped_gemm_contiguous", "grouped_gemm_kgrouped",
+              "mgg_status_string", "mgg_last_error"):
+        assert f in names
+    assert len(names) == 5, names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert lib.mgg_status_string(0) == b"ok"
+    assert lib.mgg_status_string(1) == b"invalid argument"
+    assert lib.mgg_status_string(3) == b"HIP runtime error"
+
+
+# Fake, never-dereferenced device addresses: every call below fails host validation.
+P = ctypes.c_void_p(1 << 20)
+MIS = ctypes.c_void_p((1 << 20) + 8)  # 8-byte aligned only
+NUL = None
+
+
+def masked(lib, dt=1, G=2, cap=4, N=16, K=128, A=P, SFA=P, B=P, SFB=P, sf=0, gran=0, D=P,
+           cnt=P, em=0):
+    return lib.grouped_gemm_masked(dt, G, cap, N, K, A, SFA, B, SFB, sf, gran, D, cnt, em, None)
+
+
+def contig(lib, dt=1, G=2, M=256, N=16, K=128, A=P, SFA=P, B=P, SFB=P, sf=0, gran=0, D=P,
+           idx=P, em=0):
+    return lib.grouped_gemm_contiguous(dt, G, M, N, K, A, SFA, B, SFB, sf, gran, D, idx, em, None)
+
+
+def kgrp(lib, dt=1, G=2, M=16, N=16, KT=256, A=P, SFA=P, B=P, SFB=P, sf=0, D=P, ks=P, acc=1):
+    return lib.grouped_gemm_kgrouped(dt, G, M, N, KT, A, SFA, B, SFB, sf, D, ks, acc, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), EINVAL),
+    (dict(G=0), EINVAL),
+    (dict(G=4097), EINVAL),
+    (dict(cap=0), EINVAL),
+    (dict(N=12), EINVAL),
+    (dict(N=0), EINVAL),
+    (dict(K=64), EINVAL),  # FP8 needs K % 128 == 0
+    (dict(dt=0, K=12), EINVAL),  # BF16 needs K % 8 == 0
+    (dict(A=NUL), EINVAL),
+    (dict(B=NUL), EINVAL),
+    (dict(D=NUL), EINVAL),
+    (dict(cnt=NUL), EINVAL),
+    (dict(SFA=NUL), EINVAL),
+    (dict(SFB=NUL), EINVAL),
+    (dict(A=MIS), EINVAL),
+    (dict(D=MIS), EINVAL),
+    (dict(sf=5), EINVAL),
+    (dict(gran=9), EINVAL),
+])
+def test_masked_rejects(lib, kw, code):
+    assert masked(lib, **kw) == code
+    assert lib.mgg_last_error() != b""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=0), EINVAL),
+    (dict(M=524289), EUNSUPPORTED),
+    (dict(G=0), EINVAL),
+    (dict(idx=NUL), EINVAL),
+    (dict(K=100), EINVAL),
+    (dict(B=MIS), EINVAL),
+])
+def test_contiguous_rejects(lib, kw, code):
+    assert contig(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(acc=2), EINVAL),
+    (dict(KT=-128), EINVAL),
+    (dict(KT=200), EINVAL),  # FP8 token axis must be a multiple of 128
+    (dict(G=0), EINVAL),
+    (dict(M=0), EINVAL),
+    (dict(N=4), EINVAL),
+    (dict(ks=NUL), EINVAL),
+    (dict(SFB=NUL), EINVAL),
+])
+def test_kgrouped_rejects(lib, kw, code):
+    assert kgrp(lib, **kw) == code
+
+
+def test_binding_raises_with_message_on_bad_input():
+    import torch
+    A = torch.zeros((2, 4, 128), dtype=torch.uint8)
+    with pytest.raises(ValueError):  # CPU tensors are refused before the C call
+        mgg.grouped_gemm_masked(A, A, torch.zeros((2, 4, 4), dtype=torch.bfloat16),
+                                torch.zeros(2, dtype=torch.int32))
+
+
+def test_product_path_does_not_import_the_oracle():
+    """The package and its sources never reference the oracle."""
+    pkg = os.path.join(ROOT, "moe_grouped_gemm_nt_amd")
+    for path in glob.glob(os.path.join(pkg, "**", "*"), recursive=True):
+        if os.path.isfile(path) and path.endswith((".py", ".hip", ".h", ".cpp")):
+            text = open(path).read()
+            assert "import oracle" not in text and "from oracle" not in text, path
+            assert "oracle/" not in text, path

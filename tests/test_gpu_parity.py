@@ -1,0 +1,272 @@
+"""GPU parity of the HIP path against the CPU oracle at sizes the oracle finishes in
+seconds: several tiles, ragged tails in every dimension, every dtype / scale format /
+weight-scale granularity / tile shape, boundary capacities, empty experts, sentinel
+checks of every byte outside valid rows, and tile-shape independence of the bits."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_grouped_gemm_nt_amd import synth
+from parity_util import (SENTINEL, assert_report, bf16_bits, check_contiguous, check_kgrouped,
+                         check_masked, run_contiguous, run_kgrouped, run_masked, say)
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+DEV = "cuda"
+
+
+# ----------------------------------------------------------------------------- masked
+
+
+def test_masked_bf16_pr_repro():
+    """The PR's reproduction: seed 29, G=8, cap=32, N=K=256, the printed counts, 16 calls,
+    calc_diff < 1e-5 on valid rows every time; nothing outside valid rows written."""
+    gold = json.load(open(os.path.join(GOLDEN, "masked_repro.json")))
+    say("masked bf16 repro", gold["counts"])
+    p = synth.make_masked("bf16", gold["G"], gold["cap"], gold["N"], gold["K"], gold["counts"],
+                          seed=gold["seed"], device=DEV)
+    first = None
+    for call in range(gold["calls"]):
+        D = run_masked(p, gold["expected_m"])
+        torch.cuda.synchronize()
+        rep = check_masked(p, D)
+        assert rep["calc_diff"] < gold["calc_diff_threshold"], (call, rep)
+        assert_report(rep, "bf16")
+        bits = bf16_bits(D)
+        if first is None:
+            first = bits
+        assert (bits == first).all(), f"call {call} differs from call 0"
+
+
+@pytest.mark.parametrize("dtype,sf_fmt,gran", [
+    ("bf16", "f32", "block128"),
+    ("fp8", "f32", "block128"),
+    ("fp8", "f32", "channel"),
+    ("fp8", "ue8m0", "block128"),
+    ("fp8", "ue8m0", "channel"),
+])
+def test_masked_ragged_all_tiles(dtype, sf_fmt, gran):
+    """G=5, cap=300 (not a tile multiple), N=520 (ragged last n tile), K=384 (3 slices);
+    counts cover 0, 1, partial, full. Every tile shape gives the same bits."""
+    G, cap, N, K = 5, 300, 520, 384
+    counts = [0, 1, 77, 300, 129]
+    say("masked ragged", dtype, sf_fmt, gran)
+    p = synth.make_masked(dtype, G, cap, N, K, counts, seed=3, device=DEV, sf_fmt=sf_fmt,
+                          sfb_gran=gran)
+    outs = []
+    for em in (16, 48, 200):  # picks the 32-, 64- and 128-row tiles
+        say("  expected_m", em)
+        D = run_masked(p, em)
+        torch.cuda.synchronize()
+        outs.append(bf16_bits(D))
+    rep = check_masked(p, D)
+    assert_report(rep, dtype)
+    assert (outs[0] == outs[1]).all() and (outs[1] == outs[2]).all(), "tile shapes disagree"
+
+
+def test_masked_bf16_k_tail():
+    """BF16 with K=200: the last 128-byte slice is partly past the row end."""
+    say("masked bf16 K tail")
+    p = synth.make_masked("bf16", 3, 40, 64, 200, [40, 7, 33], seed=4, device=DEV)
+    D = run_masked(p, 40)
+    torch.cuda.synchronize()
+    assert_report(check_masked(p, D), "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_masked_boundary_panel(dtype):
+    """Capacities 1..257 (not tile-divisible among them), random counts including full
+    and empty experts, a single-expert case and an all-empty case; other experts' rows
+    and padding rows keep the sentinel."""
+    gold = json.load(open(os.path.join(GOLDEN, "masked_boundary_panel.json")))
+    rng = np.random.default_rng(gold["seed"])
+    N, K = 64, 256
+    for cap in gold["capacities"]:
+        G = 4
+        counts = rng.integers(0, cap + 1, size=G)
+        counts[rng.integers(0, G)] = cap  # one full expert
+        counts[rng.integers(0, G)] = max(cap - 1, 0)  # one nearly full
+        say("boundary", dtype, "cap", cap, "counts", counts.tolist())
+        p = synth.make_masked(dtype, G, cap, N, K, counts, seed=cap, device=DEV)
+        for em in (0, cap):
+            D = run_masked(p, em)
+            torch.cuda.synchronize()
+            assert_report(check_masked(p, D), dtype)
+    say("boundary single expert", dtype)
+    p = synth.make_masked(dtype, 1, 96, N, K, [95], seed=1, device=DEV)
+    assert_report(check_masked(p, run_masked(p, 96)), dtype)
+    say("boundary all empty", dtype)
+    p = synth.make_masked(dtype, 6, 64, N, K, [0] * 6, seed=2, device=DEV)
+    D = run_masked(p, 32)
+    torch.cuda.synchronize()
+    assert (bf16_bits(D) == SENTINEL).all()
+
+
+def test_masked_out_of_range_counts_are_clamped():
+    say("masked clamp")
+    p = synth.make_masked("fp8", 3, 40, 64, 128, [40, 0, 7], seed=5, device=DEV)
+    p.counts.copy_(torch.tensor([-3, 1000, 7], dtype=torch.int32))
+    p.meta["counts"] = np.array([-3, 1000, 7])
+    D = run_masked(p, 16)
+    torch.cuda.synchronize()
+    assert_report(check_masked(p, D), "fp8")
+
+
+def test_masked_integer_exact_bitwise():
+    """Operands in {-1, 0, 1} with power-of-two scales: every sum is a small integer,
+    exact in FP32 and in bf16, so the GPU must equal the rounded oracle bit for bit."""
+    say("masked integer exact")
+    G, cap, N, K = 3, 70, 136, 256
+    rng = np.random.default_rng(8)
+    a = rng.integers(-1, 2, (G, cap, K)).astype(np.float32)
+    b = rng.integers(-1, 2, (G, N, K)).astype(np.float32)
+    A = torch.tensor(a).to(torch.float8_e4m3fn).view(torch.uint8).to(DEV)
+    B = torch.tensor(b).to(torch.float8_e4m3fn).view(torch.uint8).to(DEV)
+    SFA = torch.full((G, K // 128, cap), 0.5, device=DEV)
+    SFB = torch.full((G, 2, K // 128), 2.0, device=DEV)
+    counts = np.array([70, 3, 64], np.int32)
+    p = synth.Problem("masked", "fp8", G, N, K, A, B, SFA, SFB, cap=cap,
+                      counts=torch.tensor(counts, device=DEV), meta={"counts": counts})
+    D = run_masked(p, 64)
+    torch.cuda.synchronize()
+    ref, valid = oracle.grouped_gemm_masked("fp8", A.cpu().numpy(), B.cpu().numpy(), counts,
+                                            SFA.cpu().numpy(), SFB.cpu().numpy())
+    want = oracle.round_to_bf16(np.where(valid[..., None], ref, 0))
+    got = bf16_bits(D)
+    assert (got[valid] == want[valid]).all()
+    # the same integers as bf16 operands
+    pb = synth.Problem("masked", "bf16", G, N, K, torch.tensor(a).to(torch.bfloat16).to(DEV),
+                       torch.tensor(b).to(torch.bfloat16).to(DEV), cap=cap,
+                       counts=torch.tensor(counts, device=DEV), meta={"counts": counts})
+    D2 = run_masked(pb, 64)
+    torch.cuda.synchronize()
+    want2 = oracle.round_to_bf16(np.where(valid[..., None], ref, 0))  # same integers
+    assert (bf16_bits(D2)[valid] == want2[valid]).all()
+
+
+# ----------------------------------------------------------------------------- contiguous
+
+
+@pytest.mark.parametrize("dtype,sf_fmt,gran", [
+    ("bf16", "f32", "block128"),
+    ("fp8", "f32", "block128"),
+    ("fp8", "ue8m0", "block128"),
+    ("fp8", "ue8m0", "channel"),
+])
+def test_contiguous_ragged(dtype, sf_fmt, gran):
+    """Segments of 130, 0, 1, 127, 128 and 45 rows padded to 128, plus trailing padding
+    blocks; N=264 (ragged); every tile shape gives the same bits; padding rows keep the
+    sentinel."""
+    segs = [130, 0, 1, 127, 128, 45]
+    say("contiguous", dtype, sf_fmt, gran, segs)
+    p = synth.make_contiguous(dtype, len(segs), 264, 256, segs, seed=6, device=DEV,
+                              sf_fmt=sf_fmt, sfb_gran=gran, M_max=1152)
+    outs = []
+    for em in (8, 64, 128):
+        say("  expected_m", em)
+        D = run_contiguous(p, em)
+        torch.cuda.synchronize()
+        outs.append(bf16_bits(D))
+    assert_report(check_contiguous(p, D), dtype)
+    assert (outs[0] == outs[1]).all() and (outs[1] == outs[2]).all(), "tile shapes disagree"
+
+
+def test_contiguous_matches_masked_bitwise():
+    """The same expert rows through the masked and the contiguous entry points give
+    identical bits (same engine, same K order)."""
+    say("contiguous vs masked")
+    G, cap, N, K = 3, 128, 256, 512
+    counts = [128, 5, 77]
+    pm = synth.make_masked("fp8", G, cap, N, K, counts, seed=12, device=DEV)
+    Dm = bf16_bits(run_masked(pm, 128))
+    idx, _ = synth.contiguous_indices(counts)
+    A = torch.zeros((idx.size, K), dtype=torch.uint8, device=DEV)
+    SFA = torch.zeros((K // 128, idx.size), device=DEV)
+    r0 = 0
+    rows = []
+    for g, c in enumerate(counts):
+        A[r0:r0 + c] = pm.A[g, :c]
+        SFA[:, r0:r0 + c] = pm.SFA[g, :, :c]
+        rows.append((r0, g, c))
+        r0 += (c + 127) // 128 * 128
+    pc = synth.Problem("contiguous", "fp8", G, N, K, A, pm.B, SFA, pm.SFB, M=idx.size,
+                       m_indices=torch.tensor(idx, device=DEV),
+                       meta={"m_indices": idx, "valid_rows": sum(counts)})
+    Dc = bf16_bits(run_contiguous(pc, 64))
+    for r0, g, c in rows:
+        assert (Dc[r0:r0 + c] == Dm[g, :c]).all()
+
+
+# ----------------------------------------------------------------------------- K-grouped
+
+
+@pytest.mark.parametrize("sf_val", [1.0, 1e-4, 1e-8, 1e-30])
+def test_kgrouped_fp8_repro_shape_small(sf_val):
+    """The K-grouped repro's token split [256, 128, 128, 256] and zeroed channel at a
+    reduced channel count (M=N=256): parity, exact zeros in row 0 of the 128-token
+    experts, accumulation into a non-zero C."""
+    ks = [256, 128, 128, 256]
+    say("kgrouped fp8 small sf_val", sf_val)
+    p = synth.make_kgrouped("fp8", ks, 256, 264, seed=0, sf_val=sf_val, device=DEV)
+    C = torch.randn((4, 256, 264), device=DEV) * 1e-4
+    D = C.clone()
+    run_kgrouped(p, D, accumulate=True)
+    torch.cuda.synchronize()
+    rep = check_kgrouped(p, D, C=C)
+    assert_report(rep, "fp8")
+    D0 = run_kgrouped(p, None, accumulate=False)
+    torch.cuda.synchronize()
+    for e in (1, 2):
+        assert (D0[e, 0] == 0).all(), "zero channel must give exact zeros"
+    rep0 = check_kgrouped(p, D0)
+    assert_report(rep0, "fp8")
+
+
+def test_kgrouped_bf16_and_edge_ks():
+    """BF16 with k_e = 0, a non-multiple-of-128 count (BF16 allows multiples of 8), and
+    an out-of-contract expert that must be left untouched."""
+    ks = [0, 200, 8, 64]
+    say("kgrouped bf16", ks)
+    p = synth.make_kgrouped("bf16", ks, 72, 136, seed=2, std_a=1.0, std_b=1.0, device=DEV,
+                            K_total=288)
+    C = torch.randn((4, 72, 136), device=DEV)
+    D = C.clone()
+    run_kgrouped(p, D, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(D[0], C[0]), "k_e = 0 with accumulation leaves D_e unchanged"
+    assert_report(check_kgrouped(p, D, C=C), "bf16")
+    # out of contract: k_1 = 13 (not a multiple of 8) -> expert 1 untouched, and every
+    # later expert starts at an unaligned token offset -> untouched as well
+    bad = torch.tensor([0, 13, 8, 64], dtype=torch.int32, device=DEV)
+    D2 = C.clone()
+    import moe_grouped_gemm_nt_amd as mgg
+    mgg.grouped_gemm_kgrouped(p.A, p.B, D2, bad, 72, 136, accumulate=False)
+    torch.cuda.synchronize()
+    assert torch.equal(D2[1:], C[1:])
+    assert (D2[0] == 0).all()
+
+
+def test_kgrouped_ue8m0_scales():
+    ks = [128, 384]
+    say("kgrouped ue8m0")
+    p = synth.make_kgrouped("fp8", ks, 128, 128, seed=9, std_a=1.0, std_b=1.0, device=DEV)
+    # re-express the float scales as powers of two with codes re-quantized accordingly
+    gy, act = p.meta["grad_y"], p.meta["act"]
+    qa, sa = synth.quant_rows_1x128(gy.t().contiguous(), "ue8m0")  # [M, T] rows = channels
+    qb, sb = synth.quant_rows_1x128(act.t().contiguous(), "ue8m0")
+    A = torch.cat([qa[:, 0:128].reshape(-1), qa[:, 128:512].reshape(-1)])
+    B = torch.cat([qb[:, 0:128].reshape(-1), qb[:, 128:512].reshape(-1)])
+    pu = synth.Problem("kgrouped", "fp8", 2, 128, 512, A, B, sa, sb, "ue8m0", "channel",
+                       M=128, K_total=512, ks=p.ks, meta={"ks": np.array(ks)})
+    D = run_kgrouped(pu, None, accumulate=False)
+    torch.cuda.synchronize()
+    Dh = D.cpu().numpy()
+    ref, _ = oracle.grouped_gemm_kgrouped("fp8", A.cpu().numpy(), B.cpu().numpy(), ks, 128, 128,
+                                          512, sa.cpu().numpy(), sb.cpu().numpy(), "ue8m0")
+    assert oracle.calc_diff(Dh, ref) < 1e-3
+    assert np.allclose(Dh, ref, rtol=1e-3, atol=1e-4 * np.abs(ref).max())

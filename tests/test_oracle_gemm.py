@@ -275,8 +275,11 @@ def test_kgrouped_equals_masked_per_expert():
 
 def test_kgrouped_contract_violations_unusable():
     lay = oracle.kgrouped_layout([128, 100, -3, 256], K_total=512, granule=128)
-    assert [u for (_, _, u) in lay] == [True, False, False, True]
+    # expert 3 starts at token 228, not a multiple of 128: unusable as well
+    assert [u for (_, _, u) in lay] == [True, False, False, False]
     assert [p for (p, _, _) in lay] == [0, 128, 228, 228]
+    lay = oracle.kgrouped_layout([128, -3, 256], K_total=512, granule=128)
+    assert [u for (_, _, u) in lay] == [True, False, True]
     lay = oracle.kgrouped_layout([256, 256], K_total=384, granule=128)
     assert [u for (_, _, u) in lay] == [True, False]
 
