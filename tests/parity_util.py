@@ -7,10 +7,13 @@ from the stated acceptance bar):
     the output was filled with;
   * calc_diff against the FP64 reference rounded to bf16 (bf16 outputs) or unrounded
     (fp32 K-grouped outputs): < 1e-5 for BF16 inputs, < 1e-3 for FP8 inputs;
-  * element by element: |gpu - ref| <= 2^-8 |ref| + 1.25 K 2^-24 S + tiny, where
-    S = sum_k |a_k b_k| (the oracle run on sign-cleared codes). The first term is bf16
-    output rounding (zero for fp32 outputs), the second a first-order bound on FP32
-    accumulation over K products plus the per-128-K promotion roundings.
+  * element by element: |gpu - ref| <= 2^-8 |ref| + 1.25 K 2^-24 S [+ 2^-14 S for FP8]
+    + tiny, where S = sum_k |a_k b_k| (the oracle run on sign-cleared codes). The first
+    term is bf16 output rounding (zero for fp32 outputs), the second a first-order bound
+    on FP32 accumulation over K products plus the per-128-K promotion roundings. The
+    third covers the FP8 MFMA's own sum of 128 products, whose internal precision is
+    not published: measured on gfx950 it errs by up to about 1.3e-5 of that block's
+    sum of |products| (roughly 2^-16); 2^-14 of S keeps a 4x margin.
 """
 
 from __future__ import annotations
@@ -57,8 +60,10 @@ def tol(dtype: str) -> float:
     return 1e-5 if dtype == "bf16" else 1e-3
 
 
-def elementwise_ok(gpu: np.ndarray, ref: np.ndarray, S: np.ndarray, K: int, rounded: bool):
-    bound = (2.0 ** -8 * np.abs(ref) if rounded else 0.0) + 1.25 * K * 2.0 ** -24 * S + 1e-30
+def elementwise_ok(gpu: np.ndarray, ref: np.ndarray, S: np.ndarray, K: int, rounded: bool,
+                   fp8: bool):
+    bound = ((2.0 ** -8 * np.abs(ref) if rounded else 0.0) + 1.25 * K * 2.0 ** -24 * S
+             + (2.0 ** -14 * S if fp8 else 0.0) + 1e-30)
     err = np.abs(gpu - ref)
     bad = ~(err <= bound)
     return int(bad.sum()), float(np.max(err / bound)) if err.size else 0.0
@@ -114,7 +119,7 @@ def check_masked(p: synth.Problem, D: torch.Tensor, experts=None, rows=None, col
         gpu = oracle.decode_bf16(Dh[g][np.ix_(sel_rows, cc)])
         r = ref[np.ix_(sel_rows, cc)]
         s = S[np.ix_(sel_rows, cc)]
-        nb, w = elementwise_ok(gpu, r, s, p.K, rounded=True)
+        nb, w = elementwise_ok(gpu, r, s, p.K, rounded=True, fp8=p.dtype == "fp8")
         n_bad += nb
         worst = max(worst, w)
         all_gpu.append(gpu.ravel())
@@ -172,7 +177,7 @@ def check_contiguous(p: synth.Problem, D: torch.Tensor, rows=None, cols=None,
                                               p.sfb_gran, p.sf_fmt, cols=cc)
         ref, S = ref[:, cc], S[:, cc]
         gpu = oracle.decode_bf16(Dh[np.ix_(r_idx, cc)])
-        nb, w = elementwise_ok(gpu, ref, S, p.K, rounded=True)
+        nb, w = elementwise_ok(gpu, ref, S, p.K, rounded=True, fp8=p.dtype == "fp8")
         n_bad += nb
         worst = max(worst, w)
         all_gpu.append(gpu.ravel())
@@ -218,7 +223,8 @@ def check_kgrouped(p: synth.Problem, D: torch.Tensor, C=None, experts=None, rows
         gpu = Dh[e][np.ix_(rr, cc)].astype(np.float64)
         r = ref[e][np.ix_(rr, cc)]
         s = S[e][np.ix_(rr, cc)]
-        nb, w = elementwise_ok(gpu, r, s, max(ks[e], 1) + 2, rounded=False)
+        nb, w = elementwise_ok(gpu, r, s, max(ks[e], 1) + 2, rounded=False,
+                              fp8=p.dtype == "fp8")
         n_bad += nb
         worst = max(worst, w)
         all_gpu.append(gpu.ravel())
