@@ -90,6 +90,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "copy_calibration":
+        copy_calibration(dev, args)
+        return
     mgg.load_library()
     p, opt = synth.make_workload(args.workload, dev)
     flops = p.valid_flops()
@@ -195,6 +198,28 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def copy_calibration(dev, args):
+    """A plain device-to-device copy of 256 MiB, for scaling the HBM byte counters: the
+    copy reads and writes exactly 256 MiB per launch."""
+    import torch
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(max(args.warmup, 1)):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize(dev)
+    ms = t0.elapsed_time(t1) / args.steps
+    print(json.dumps({"workload": "copy_calibration", "bytes_read": n, "bytes_written": n,
+                      "ms_per_copy": round(ms, 5), "GBps_read_plus_write": round(2 * n / ms / 1e6, 1)}),
+          flush=True)
 
 
 def cpu_baseline(p, opt, flops, target_s):

@@ -47,8 +47,9 @@ constexpr int kThreads = 256;
 constexpr int kSliceBytes = 128;  // K bytes per row per pipeline stage
 constexpr int kXcds = 8;          // MI355X: 8 accelerator dies, WGs dispatched round-robin
 constexpr int kContigBlock = 128; // rows per contiguous-layout alignment block
-constexpr int kMaxExperts = 4096;
+constexpr int kMaxExperts = 4096;  // the expert index shares an int with the block index
 constexpr int kMaxContigBlocks = 4096;
+constexpr int kLdsBytes = 160 * 1024;  // per workgroup on gfx950
 
 struct Params {
   const uint8_t* A;
@@ -63,20 +64,22 @@ struct Params {
   int K;        // masked, contiguous: K; K-grouped: K_total
   int accumulate;  // K-grouped: 1 adds the product to D
   int k_granule;   // K-grouped: required multiple of k_e (128 FP8, 8 BF16)
+  uint32_t sfa_bytes, sfb_bytes;  // readable bytes of the scale tensors (FP8)
+  uint32_t meta_bytes;            // bytes of the routing tensor
 };
 
 // Tile configuration: BM activation rows x BN weight rows per workgroup; 4 waves laid
-// out WM (along m) x WN (along n).
-template <int BM_, int BN_, int WM_, int WN_>
+// out WM (along m) x WN (along n); S pipeline stages of 128-byte K slices in LDS.
+template <int BM_, int BN_, int WM_, int WN_, int S_>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_;
   static_assert(WM * WN == 4, "four waves per workgroup");
+  static_assert(S >= 2 && S <= 6, "pipeline depth");
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int MJ = WTM / 16, NI = WTN / 16;
-  static_assert(MJ >= 1 && NI >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "16x16 subtiles");
+  static_assert(MJ >= 1 && NI >= 2 && WTM % 16 == 0 && WTN % 16 == 0, "16x16 subtiles");
   static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's n range stays in one 128-row block");
-  static constexpr int CHUNKS = (BM + BN) * (kSliceBytes / 16);
-  static constexpr int CH_PER_THREAD = (CHUNKS + kThreads - 1) / kThreads;
+  static_assert((BM + BN) % 32 == 0 && BM % 8 == 0, "whole 8-row copies, 4 waves");
 };
 
 // ----------------------------------------------------------------------------- helpers
@@ -108,30 +111,33 @@ __device__ __forceinline__ float load_scale(const void* base, long idx) {
 }
 
 // Exclusive scan of `n` ints held in LDS `buf` (in place), block-wide; returns the total.
-// Every thread of the block must call it.
+// Every thread of the block must call it; `s_tmp` needs 4 ints. Each thread sums a
+// contiguous chunk, waves scan their 64 partial sums with cross-lane shuffles, and the
+// four wave totals are combined through LDS (two barriers in all).
 __device__ int block_exclusive_scan(int* buf, int n, int* s_tmp) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (n + kThreads - 1) / kThreads;
   const int lo = tid * per;
   const int hi = min(lo + per, n);
   int local = 0;
   for (int i = lo; i < hi; ++i) local += buf[i];
-  s_tmp[tid] = local;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the 256 partial sums.
-  for (int off = 1; off < kThreads; off <<= 1) {
-    int v = (tid >= off) ? s_tmp[tid - off] : 0;
-    __syncthreads();
-    s_tmp[tid] += v;
-    __syncthreads();
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
   }
-  int run = s_tmp[tid] - local;  // exclusive prefix of this thread's range
+  if (lane == 63) s_tmp[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += s_tmp[w];
+  const int total = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
+  int run = before + incl - local;  // exclusive prefix of this thread's chunk
   for (int i = lo; i < hi; ++i) {
-    int v = buf[i];
+    const int v = buf[i];
     buf[i] = run;
     run += v;
   }
-  int total = s_tmp[kThreads - 1];
   __syncthreads();
   return total;
 }
@@ -151,6 +157,91 @@ __device__ __forceinline__ int weight_lds_row(int n) {
 // that 8 consecutive rows read at the same logical chunk hit 8 different bank groups.
 __device__ __forceinline__ int swz(int row, int c) {
   return row * kSliceBytes + ((c ^ (row & 7)) << 4);
+}
+
+// Inverse of weight_lds_row: the tile-local weight row stored in LDS row R.
+template <class T>
+__device__ __forceinline__ int weight_row_of_lds(int R) {
+  const int w = R / T::WTN, rl = R % T::WTN;
+  const int i = rl / 16, q = (rl % 16) / 4, r = rl % 4;
+  return w * T::WTN + q * 4 * T::NI + 4 * i + r;
+}
+
+// ----------------------------------------------------------------------------- buffers
+//
+// Global memory is read through buffer resources (base, size in bytes): a lane whose
+// byte offset is at or beyond the size reads zeros and its stores are dropped. Every
+// out-of-range row, column or K chunk is expressed that way (offset kOOB), so nothing
+// outside an expert's block is ever touched and the instruction stream is the same for
+// every lane and every tile.
+
+constexpr uint32_t kOOB = 0x80000000u;  // beyond any resource size (sizes are < 2^31)
+
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t nbytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  v4i r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(a & 0xffffffffu));
+  r.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));  // stride 0
+  r.z = __builtin_amdgcn_readfirstlane((int)nbytes);
+  r.w = 0x00020000;  // raw 32-bit data, gfx9 buffer format
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// Direct global -> LDS copies: each lane's 16 (or 4) bytes land at lds + 16 * lane
+// (or 4 * lane). The s_nops cover the SGPR-write -> VMEM-read and M0-write -> LDS-DMA
+// wait states, which the compiler cannot see inside the asm.
+// The LDS address is uniform by construction; readfirstlane makes that explicit. A
+// batch of copies starts with dma_fence(), which covers the wait states between a
+// VALU write of an SGPR (resource descriptors come from readfirstlane) and a vector
+// memory instruction reading it; each copy then only needs the M0 -> LDS-DMA gap.
+__device__ __forceinline__ void dma_fence() { asm volatile("s_nop 4" ::: "memory"); }
+__device__ __forceinline__ void dma_x4(uint32_t lds, v4i rsrc, uint32_t voff) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(l), "v"(voff), "s"(rsrc) : "memory");
+}
+__device__ __forceinline__ void dma_x1(uint32_t lds, v4i rsrc, uint32_t voff) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(l), "v"(voff), "s"(rsrc) : "memory");
+}
+// Pins a uniform value in SGPRs at this point of the program.
+__device__ __forceinline__ void pin_sgpr(v4i& r) { asm volatile("" : "+s"(r)); }
+
+// Workgroup barrier that orders LDS: all of this wave's LDS reads have returned and no
+// memory access is moved across it by the compiler.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(BASE + k * STEP) for a run-time k in [0, KMAX] (uniform); vmcnt
+// holds at most 63, and a smaller count than needed only waits longer.
+template <int N>
+__device__ __forceinline__ void vm_wait_imm() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N < 63 ? N : 63) : "memory");
+}
+template <int BASE, int STEP, int K>
+__device__ __forceinline__ void vm_wait_steps(int k) {
+  if constexpr (K == 0) {
+    vm_wait_imm<BASE>();
+  } else {
+    if (k >= K) vm_wait_imm<BASE + K * STEP>();
+    else vm_wait_steps<BASE, STEP, K - 1>(k);
+  }
+}
+
+// The LLVM raw buffer store intrinsic, declared with the 128-bit resource as a plain
+// int vector so the same descriptor serves the asm copies above.
+extern "C" __device__ void mgg_raw_buffer_store_v4i32(v4i vdata, v4i rsrc, int voffset,
+                                                     int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.store.v4i32");
+
+__device__ __forceinline__ void store_b128(v4i rsrc, uint32_t voff, v4i v) {
+  mgg_raw_buffer_store_v4i32(v, rsrc, (int)voff, 0, 0);
 }
 
 }  // namespace mgg

@@ -24,23 +24,24 @@ mgg_status fail(mgg_status s, const std::string& msg) {
   return s;
 }
 
-// Tile shapes. Small-M tiles keep the MFMA work proportional to the valid rows when
-// experts receive few tokens; all of them produce bitwise-identical results.
-using TileS = Tile<32, 256, 1, 4>;   // <= 32 rows per expert: weight streaming
-using TileM = Tile<64, 256, 1, 4>;   // <= 64 rows
-using TileL = Tile<128, 256, 2, 2>;  // larger experts
-using TileK = Tile<128, 128, 2, 2>;  // K-grouped output tiles
+// Tile shapes (BM activation rows x BN weight rows, 4 waves, S pipeline stages). The
+// small-M shapes keep MFMA work proportional to the valid rows and put more
+// workgroups on the weight stream when experts receive few tokens; all of them
+// produce bitwise-identical results.
+using TileS = Tile<32, 64, 2, 2, 4>;    // <= 32 rows per expert
+using TileM = Tile<64, 128, 2, 2, 3>;   // <= 64 rows
+using TileL = Tile<128, 256, 2, 2, 3>;  // larger experts
+using TileK = Tile<64, 64, 2, 2, 4>;    // K-grouped output tiles
 
 enum TileId { kTileS = 0, kTileM = 1, kTileL = 2 };
 
 struct DevInfo {
   int cus = 0;
-  int max_lds = 0;
 };
 
 std::mutex g_mu;
 std::unordered_map<int, DevInfo> g_dev;
-std::unordered_map<const void*, int> g_occ;  // (kernel) -> resident workgroups per CU
+std::unordered_map<const void*, int> g_occ;  // kernel -> resident workgroups per CU
 
 bool dev_info(DevInfo* out) {
   int dev = 0;
@@ -54,39 +55,55 @@ bool dev_info(DevInfo* out) {
   DevInfo d;
   if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return false;
-  if (hipDeviceGetAttribute(&d.max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
-      hipSuccess)
-    return false;
   g_dev[dev] = d;
   *out = d;
   return true;
 }
 
-template <class T, int VAR, int DT, int SF, int GRAN>
-constexpr int pipe_bytes() {
-  return Layout<T, VAR, DT, SF, GRAN>::PIPE;
+long cdiv(long a, long b) { return (a + b - 1) / b; }
+
+// Bytes the scheduler keeps in LDS after the pipeline stages, and the transient scan
+// scratch it needs inside the stages.
+template <int VAR>
+void sched_bytes(const Params& p, long* persistent, long* transient) {
+  if (VAR == kContig) {
+    const long nb = cdiv(p.rows, kContigBlock);
+    *persistent = nb * 4;
+    *transient = (kThreads + nb) * 4;
+  } else {
+    *persistent = 2L * p.G * 4;
+    *transient = kThreads * 4;
+  }
 }
 
-template <class T, int VAR, int DT, int SF, int GRAN>
-mgg_status launch(const Params& p, long max_tiles, int sched_n, hipStream_t stream) {
-  auto kern = grouped_gemm_kernel<T, VAR, DT, SF, GRAN>;
-  const size_t lds = (size_t)pipe_bytes<T, VAR, DT, SF, GRAN>() +
-                     (size_t)(kThreads + 3 * sched_n) * sizeof(int);
+template <class T, int VAR, int DT, int SF, int GRAN, bool ACC>
+long lds_bytes(const Params& p) {
+  long pers, trans;
+  sched_bytes<VAR>(p, &pers, &trans);
+  const long pipe = Layout<T, VAR, DT, SF, GRAN, ACC>::PIPE;
+  if (trans > pipe) return 1L << 40;
+  return pipe + pers;
+}
+
+template <class T, int VAR, int DT, int SF, int GRAN, bool ACC>
+mgg_status launch(const Params& p, long max_tiles, hipStream_t stream) {
+  auto kern = grouped_gemm_kernel<T, VAR, DT, SF, GRAN, ACC>;
+  const long lds = lds_bytes<T, VAR, DT, SF, GRAN, ACC>(p);
+  if (lds > kLdsBytes)
+    return fail(MGG_EUNSUPPORTED, "too many experts or row blocks for the LDS scheduler");
   DevInfo dev;
   if (!dev_info(&dev)) return fail(MGG_EHIP, "hipGetDevice/hipDeviceGetAttribute failed");
-  if ((long)lds > 160 * 1024)
-    return fail(MGG_EUNSUPPORTED, "too many experts or row blocks for the LDS scheduler");
   int occ = 1;
   {
     std::lock_guard<std::mutex> lk(g_mu);
     auto it = g_occ.find((const void*)kern);
     if (it == g_occ.end()) {
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          160 * 1024);
+      if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              kLdsBytes) != hipSuccess)
+        return fail(MGG_EHIP, "hipFuncSetAttribute failed");
+      // Residency at the pipeline's own footprint plus a typical scheduler table.
       int o = 0;
-      // Occupancy at the pipeline's own LDS footprint; the scheduler arrays are small
-      // for typical expert counts.
-      const size_t lds_typ = (size_t)pipe_bytes<T, VAR, DT, SF, GRAN>() + 4096;
+      const size_t lds_typ = (size_t)Layout<T, VAR, DT, SF, GRAN, ACC>::PIPE + 4096;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, kThreads, lds_typ) !=
               hipSuccess || o < 1)
         o = 1;
@@ -100,33 +117,42 @@ mgg_status launch(const Params& p, long max_tiles, int sched_n, hipStream_t stre
   long grid = max_tiles < resident ? max_tiles : resident;
   if (grid >= kXcds) grid -= grid % kXcds;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, stream, p);
-  hipError_t e = hipGetLastError();
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), (size_t)lds, stream, p);
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MGG_EHIP, std::string("kernel launch: ") + hipGetErrorString(e));
   return MGG_OK;
+}
+
+template <class T, int VAR>
+long m_tiles(const Params& p) {
+  const long ntn = cdiv(p.N, T::BN);
+  if (VAR == kMasked) return (long)p.G * cdiv(p.rows, T::BM) * ntn;
+  return cdiv(p.rows, kContigBlock) * (kContigBlock / T::BM) * ntn;
+}
+
+template <int VAR, int DT, int SF, int GRAN>
+mgg_status launch_tile(TileId tile, const Params& p, hipStream_t s) {
+  // The largest tile needs the most LDS; fall back to the middle one when the
+  // scheduler table does not fit next to it.
+  if (tile == kTileL && lds_bytes<TileL, VAR, DT, SF, GRAN, false>(p) > kLdsBytes) tile = kTileM;
+  switch (tile) {
+    case kTileS: return launch<TileS, VAR, DT, SF, GRAN, false>(p, m_tiles<TileS, VAR>(p), s);
+    case kTileM: return launch<TileM, VAR, DT, SF, GRAN, false>(p, m_tiles<TileM, VAR>(p), s);
+    default: return launch<TileL, VAR, DT, SF, GRAN, false>(p, m_tiles<TileL, VAR>(p), s);
+  }
 }
 
 // Dispatch over the compile-time parameters of the M-grouped variants.
 template <int VAR>
 mgg_status dispatch_m(mgg_dtype dt, mgg_sf_fmt sf, mgg_sfb_gran gran, TileId tile,
-                      const Params& p, long tiles_s, long tiles_m, long tiles_l, int sched_n,
-                      hipStream_t s) {
-#define MGG_TILE_SWITCH(DT_, SF_, GR_)                                                  \
-  switch (tile) {                                                                       \
-    case kTileS: return launch<TileS, VAR, DT_, SF_, GR_>(p, tiles_s, sched_n, s);      \
-    case kTileM: return launch<TileM, VAR, DT_, SF_, GR_>(p, tiles_m, sched_n, s);      \
-    default: return launch<TileL, VAR, DT_, SF_, GR_>(p, tiles_l, sched_n, s);          \
-  }
-  if (dt == MGG_BF16) {
-    MGG_TILE_SWITCH(kBF16, kSfF32, kSfbBlock)
-  }
+                      const Params& p, hipStream_t s) {
+  if (dt == MGG_BF16) return launch_tile<VAR, kBF16, kSfF32, kSfbBlock>(tile, p, s);
   if (sf == MGG_SF_F32) {
-    if (gran == MGG_SFB_BLOCK128) { MGG_TILE_SWITCH(kFP8, kSfF32, kSfbBlock) }
-    MGG_TILE_SWITCH(kFP8, kSfF32, kSfbChannel)
+    if (gran == MGG_SFB_BLOCK128) return launch_tile<VAR, kFP8, kSfF32, kSfbBlock>(tile, p, s);
+    return launch_tile<VAR, kFP8, kSfF32, kSfbChannel>(tile, p, s);
   }
-  if (gran == MGG_SFB_BLOCK128) { MGG_TILE_SWITCH(kFP8, kSfUE8M0, kSfbBlock) }
-  MGG_TILE_SWITCH(kFP8, kSfUE8M0, kSfbChannel)
-#undef MGG_TILE_SWITCH
+  if (gran == MGG_SFB_BLOCK128) return launch_tile<VAR, kFP8, kSfUE8M0, kSfbBlock>(tile, p, s);
+  return launch_tile<VAR, kFP8, kSfUE8M0, kSfbChannel>(tile, p, s);
 }
 
 TileId pick_tile(int expected_m, int fallback) {
@@ -136,9 +162,17 @@ TileId pick_tile(int expected_m, int fallback) {
   return kTileL;
 }
 
-long cdiv(long a, long b) { return (a + b - 1) / b; }
-
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Every buffer the kernels address must be below 2 GiB so that a 32-bit out-of-range
+// offset can mask a lane.
+constexpr long kMaxBuffer = (1L << 31) - 1;
+
+uint32_t scale_bytes(long count, mgg_sf_fmt sf) {
+  // UE8M0 buffers are read in whole dwords: the caller's allocation must be readable up
+  // to the next multiple of 4 bytes.
+  return (uint32_t)(sf == MGG_SF_F32 ? count * 4 : (count + 3) / 4 * 4);
+}
 
 mgg_status check_common(mgg_dtype dt, int N, int K, const void* A, const void* SFA,
                         const void* B, const void* SFB, mgg_sf_fmt sf, const void* D,
@@ -155,10 +189,15 @@ mgg_status check_common(mgg_dtype dt, int N, int K, const void* A, const void* S
   if (dt == MGG_FP8_E4M3) {
     if (!SFA || !SFB) return fail(MGG_EINVAL, "FP8 needs SFA and SFB");
     if (sf != MGG_SF_F32 && sf != MGG_SF_UE8M0) return fail(MGG_EINVAL, "unknown scale format");
-    if (sf == MGG_SF_F32 && (!aligned(SFA, 4) || !aligned(SFB, 4)))
-      return fail(MGG_EINVAL, "float32 scales must be 4-byte aligned");
+    if (!aligned(SFA, 4) || !aligned(SFB, 4)) return fail(MGG_EINVAL, "scales must be 4-byte aligned");
   }
   if (!aligned(meta, 4)) return fail(MGG_EINVAL, "routing buffer must be 4-byte aligned");
+  return MGG_OK;
+}
+
+mgg_status check_sizes(std::initializer_list<long> sizes) {
+  for (long s : sizes)
+    if (s > kMaxBuffer) return fail(MGG_EUNSUPPORTED, "an operand block exceeds 2 GiB");
   return MGG_OK;
 }
 
@@ -189,11 +228,12 @@ mgg_status grouped_gemm_masked(mgg_dtype dt, int G, int cap, int N, int K, const
   if (cap < 1) return fail(MGG_EINVAL, "cap must be positive");
   if (dt == MGG_FP8_E4M3 && gran != MGG_SFB_BLOCK128 && gran != MGG_SFB_CHANNEL)
     return fail(MGG_EINVAL, "unknown weight-scale granularity");
-  const long ntn_s = cdiv(N, TileS::BN), ntn_l = cdiv(N, TileL::BN);
-  const long tiles_s = (long)G * cdiv(cap, TileS::BM) * ntn_s;
-  const long tiles_m = (long)G * cdiv(cap, TileM::BM) * ntn_s;
-  const long tiles_l = (long)G * cdiv(cap, TileL::BM) * ntn_l;
-  if (tiles_s >= (1L << 31)) return fail(MGG_EUNSUPPORTED, "problem too large");
+  const long esz = dt == MGG_FP8_E4M3 ? 1 : 2, KB = K / 128, NB = cdiv(N, 128);
+  const long sfa_n = (long)G * KB * cap;
+  const long sfb_n = gran == MGG_SFB_BLOCK128 ? (long)G * NB * KB : (long)G * KB * N;
+  st = check_sizes({(long)cap * K * esz, (long)N * K * esz, (long)cap * N * 2, sfa_n * 4,
+                    sfb_n * 4, (long)G * cdiv(cap, 32) * cdiv(N, 64)});
+  if (st != MGG_OK) return st;
   Params p{};
   p.A = (const uint8_t*)A;
   p.B = (const uint8_t*)B;
@@ -205,8 +245,10 @@ mgg_status grouped_gemm_masked(mgg_dtype dt, int G, int cap, int N, int K, const
   p.rows = cap;
   p.N = N;
   p.K = K;
-  const TileId tile = pick_tile(expected_m, cap);
-  return dispatch_m<kMasked>(dt, sf, gran, tile, p, tiles_s, tiles_m, tiles_l, G, stream);
+  p.sfa_bytes = dt == MGG_FP8_E4M3 ? scale_bytes(sfa_n, sf) : 0;
+  p.sfb_bytes = dt == MGG_FP8_E4M3 ? scale_bytes(sfb_n, sf) : 0;
+  p.meta_bytes = (uint32_t)G * 4;
+  return dispatch_m<kMasked>(dt, sf, gran, pick_tile(expected_m, cap), p, stream);
 }
 
 mgg_status grouped_gemm_contiguous(mgg_dtype dt, int G, int M, int N, int K, const void* A,
@@ -217,16 +259,16 @@ mgg_status grouped_gemm_contiguous(mgg_dtype dt, int G, int M, int N, int K, con
   g_last_error.clear();
   mgg_status st = check_common(dt, N, K, A, SFA, B, SFB, sf, D, m_indices);
   if (st != MGG_OK) return st;
-  if (G < 1) return fail(MGG_EINVAL, "G must be positive");
+  if (G < 1 || G > kMaxExperts) return fail(MGG_EINVAL, "G must be in [1, 4096]");
   if (M < 1 || M > kMaxContigBlocks * kContigBlock)
     return fail(M < 1 ? MGG_EINVAL : MGG_EUNSUPPORTED, "M must be in [1, 524288]");
   if (dt == MGG_FP8_E4M3 && gran != MGG_SFB_BLOCK128 && gran != MGG_SFB_CHANNEL)
     return fail(MGG_EINVAL, "unknown weight-scale granularity");
-  const long nb = cdiv(M, kContigBlock);
-  const long ntn_s = cdiv(N, TileS::BN), ntn_l = cdiv(N, TileL::BN);
-  const long tiles_s = nb * (kContigBlock / TileS::BM) * ntn_s;
-  const long tiles_m = nb * (kContigBlock / TileM::BM) * ntn_s;
-  const long tiles_l = nb * (kContigBlock / TileL::BM) * ntn_l;
+  const long esz = dt == MGG_FP8_E4M3 ? 1 : 2, KB = K / 128, NB = cdiv(N, 128);
+  const long sfa_n = KB * M;
+  const long sfb_n = gran == MGG_SFB_BLOCK128 ? (long)G * NB * KB : (long)G * KB * N;
+  st = check_sizes({(long)M * K * esz, (long)N * K * esz, (long)M * N * 2, sfa_n * 4, sfb_n * 4});
+  if (st != MGG_OK) return st;
   Params p{};
   p.A = (const uint8_t*)A;
   p.B = (const uint8_t*)B;
@@ -238,8 +280,10 @@ mgg_status grouped_gemm_contiguous(mgg_dtype dt, int G, int M, int N, int K, con
   p.rows = M;
   p.N = N;
   p.K = K;
-  const TileId tile = pick_tile(expected_m, kContigBlock);
-  return dispatch_m<kContig>(dt, sf, gran, tile, p, tiles_s, tiles_m, tiles_l, (int)nb, stream);
+  p.sfa_bytes = dt == MGG_FP8_E4M3 ? scale_bytes(sfa_n, sf) : 0;
+  p.sfb_bytes = dt == MGG_FP8_E4M3 ? scale_bytes(sfb_n, sf) : 0;
+  p.meta_bytes = (uint32_t)M * 4;
+  return dispatch_m<kContig>(dt, sf, gran, pick_tile(expected_m, kContigBlock), p, stream);
 }
 
 mgg_status grouped_gemm_kgrouped(mgg_dtype dt, int G, int M, int N, int K_total, const void* A,
@@ -255,8 +299,11 @@ mgg_status grouped_gemm_kgrouped(mgg_dtype dt, int G, int M, int N, int K_total,
   if (G < 1 || G > kMaxExperts) return fail(MGG_EINVAL, "G must be in [1, 4096]");
   if (M < 1) return fail(MGG_EINVAL, "M must be positive");
   if (accumulate != 0 && accumulate != 1) return fail(MGG_EINVAL, "accumulate must be 0 or 1");
+  const long esz = dt == MGG_FP8_E4M3 ? 1 : 2, KB = K_total / 128;
   const long tiles = (long)G * cdiv(M, TileK::BM) * cdiv(N, TileK::BN);
-  if (tiles >= (1L << 31)) return fail(MGG_EUNSUPPORTED, "problem too large");
+  st = check_sizes({(long)M * K_total * esz, (long)N * K_total * esz, (long)M * N * 4,
+                    KB * M * 4, KB * N * 4, tiles});
+  if (st != MGG_OK) return st;
   Params p{};
   p.A = (const uint8_t*)A;
   p.B = (const uint8_t*)B;
@@ -270,11 +317,16 @@ mgg_status grouped_gemm_kgrouped(mgg_dtype dt, int G, int M, int N, int K_total,
   p.K = K_total;
   p.accumulate = accumulate;
   p.k_granule = dt == MGG_FP8_E4M3 ? 128 : 8;
-  if (dt == MGG_BF16)
-    return launch<TileK, kKGrouped, kBF16, kSfF32, kSfbChannel>(p, tiles, G, stream);
-  if (sf == MGG_SF_F32)
-    return launch<TileK, kKGrouped, kFP8, kSfF32, kSfbChannel>(p, tiles, G, stream);
-  return launch<TileK, kKGrouped, kFP8, kSfUE8M0, kSfbChannel>(p, tiles, G, stream);
+  p.sfa_bytes = dt == MGG_FP8_E4M3 ? scale_bytes(KB * M, sf) : 0;
+  p.sfb_bytes = dt == MGG_FP8_E4M3 ? scale_bytes(KB * N, sf) : 0;
+  p.meta_bytes = (uint32_t)G * 4;
+#define MGG_KG(DT_, SF_)                                                              \
+  return accumulate ? launch<TileK, kKGrouped, DT_, SF_, kSfbChannel, true>(p, tiles, stream) \
+                    : launch<TileK, kKGrouped, DT_, SF_, kSfbChannel, false>(p, tiles, stream)
+  if (dt == MGG_BF16) { MGG_KG(kBF16, kSfF32); }
+  if (sf == MGG_SF_F32) { MGG_KG(kFP8, kSfF32); }
+  MGG_KG(kFP8, kSfUE8M0);
+#undef MGG_KG
 }
 
 }  // extern "C"

@@ -1,47 +1,107 @@
-// grouped_gemm_kernel.h - the persistent grouped NT GEMM kernel template (see
-// gemm_engine.h for the design). Included by exactly one translation unit, which
-// instantiates it for every (variant, dtype, scale format, weight-scale granularity,
-// tile) combination the host dispatcher can pick.
+// grouped_gemm_kernel.h - the persistent grouped NT GEMM kernel template (the design is
+// described in gemm_engine.h). Included by exactly one translation unit, which
+// instantiates it for every (tile, variant, dtype, scale format, weight-scale
+// granularity, accumulation) combination the host dispatcher can pick.
+//
+// Pipeline. A workgroup walks a flat sequence of work items (tile, 128-byte K slice).
+// Two cursors run over the same sequence: the issue cursor starts the direct
+// global -> LDS copies of item i + S - 1 into ring stage (i + S - 1) % S while the
+// compute cursor runs the MFMAs of item i from stage i % S. Each wave issues the same
+// number of copy instructions for every item (out-of-range lanes and idle items copy
+// zeros), and every store of the epilogue is issued unconditionally (masked lanes use
+// an out-of-range offset), so each wave knows exactly how many of its vector-memory
+// operations are younger than the copies of item i and waits for exactly those
+// (vmcnt counts in issue order). One barrier per item then makes every wave's copies
+// visible and guarantees the stage about to be refilled is no longer being read.
 #pragma once
 
 #include "gemm_engine.h"
 
 namespace mgg {
 
-// Everything a workgroup needs to run one output tile. All fields are uniform across
-// the workgroup.
+// Everything a workgroup needs to run one output tile. All fields are uniform.
 struct TileCtx {
-  int valid;    // 0 once the workgroup has no more tiles
-  int g;        // expert
-  int m0, n0;   // first activation row / weight row of the tile
-  int nk;       // 128-byte K slices to run (at least 1)
-  int k_bytes;  // bytes of K in every operand row (0: nothing to load)
-  int a_lim;    // activation rows < a_lim are loaded (others read as zero)
-  int row_end;  // masked: valid rows end; contiguous/K-grouped: M
-  long a_off;   // byte offset of the expert's activation block
-  long b_off;   // byte offset of the expert's weight block
-  int lda, ldb; // row strides in bytes
-  long sfa_off; // element offset of scale group 0 for row 0
-  int sfa_ld;   // elements between consecutive scale groups
+  int valid;     // 0 once the workgroup has no more tiles
+  int g;         // expert
+  int m0, n0;    // first activation row / weight row of the tile
+  int nk;        // 128-byte K slices to run (at least 1)
+  int k_bytes;   // bytes of K in every operand row (0: nothing to load)
+  int a_lim;     // activation rows < a_lim are loaded (others read as zero)
+  int row_end;   // masked: valid rows end; contiguous/K-grouped: M
+  const uint8_t* a_base;  // expert's activation block
+  uint32_t a_bytes;
+  const uint8_t* b_base;  // expert's weight block
+  uint32_t b_bytes;
+  int lda, ldb;  // row strides in bytes
+  long sfa_off;  // element offset of scale group 0, row 0
+  int sfa_ld;    // elements between consecutive scale groups
   long sfb_off;
   int sfb_ld;
-  long d_row0;  // output element offset of row 0 of the expert's output block
+  uint8_t* d_base;  // expert's output block
+  uint32_t d_bytes;
 };
 
 template <class T, int VAR>
 struct Sched {
-  // LDS scheduler arrays (allocated after the pipeline stages).
-  int* s_a;    // masked: tile prefix [G]; contiguous: block flags/prefix; K-grouped: p_e
-  int* s_b;    // masked: clamped counts; contiguous: block experts; K-grouped: usable k_e
-  int* s_c;    // contiguous: list of valid blocks
-  int* s_tmp;  // scan scratch [256]
+  int* s_a;    // masked: tile prefix [G]; K-grouped: p_e [G]
+  int* s_b;    // masked: clamped counts [G]; contiguous: packed (block << 12 | expert) of
+               // each valid block; K-grouped: usable k_e or -1 [G]
   int total;   // number of tiles
   int ntn;     // n tiles per expert
   int mtn;     // K-grouped: m tiles per expert
 };
 
+// LDS layout of one pipeline stage. Every region is a whole number of copy
+// instructions (1 KB for 16-byte copies, 256 B for 4-byte copies).
+template <class T, int VAR, int DT, int SF, int GRAN, bool ACC>
+struct Layout {
+  static constexpr bool FP8 = DT == kFP8;
+  static constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+  static constexpr int AB_INSTR = (T::BM + T::BN) / 8;  // 8 rows of 128 B per copy
+  // Scale runs: float32 -> one lane per scale; UE8M0 -> one lane per aligned dword of
+  // the byte run (the run may start anywhere inside a dword).
+  static constexpr int SA_LANES = FP8 ? (SF == kSfF32 ? T::BM : T::BM / 4 + 2) : 0;
+  static constexpr int SBN_BLOCK = T::BN >= 128 ? T::BN / 128 : 1;
+  static constexpr int SB_LANES =
+      FP8 ? (GRAN == kSfbChannel ? (SF == kSfF32 ? T::BN : T::BN / 4 + 2) : SBN_BLOCK) : 0;
+  static constexpr int SA_INSTR = cdiv(SA_LANES, 64);
+  static constexpr int SB_INSTR = cdiv(SB_LANES, 64);
+  static constexpr int RI_INSTR = VAR == kContig ? cdiv(T::BM, 64) : 0;
+  static constexpr int C_ROW_CHUNKS = T::BN / 4;  // 16-byte chunks per fp32 output row
+  static constexpr int C_INSTR = ACC ? T::BM * T::BN * 4 / 1024 : 0;
+  // Copy slots per wave. Operand rows: slot u of wave w copies rows 8(4u + w) ..
+  // 8(4u + w) + 7 of the [A; B] tile, so A and B slots are fixed per u (BM % 32 == 0).
+  // Scale and row-index copies are few: they are dealt to the four waves ("small"
+  // slots, padded with a dummy copy). Accumulation-input copies take U_C whole slots.
+  static constexpr int U_A = T::BM / 32, U_B = T::BN / 32, U_AB = U_A + U_B;
+  static constexpr int SMALL = SA_INSTR + SB_INSTR + RI_INSTR;
+  static constexpr int U_SM = cdiv(SMALL, 4);
+  static_assert(C_INSTR % 4 == 0, "accumulation-input copies split evenly over 4 waves");
+  static constexpr int U_C = C_INSTR / 4;
+  static constexpr int PER_WAVE = U_AB + U_SM + U_C;  // copy instructions per wave per item
+  static constexpr bool HAS_DUMMY = U_SM * 4 > SMALL;
+
+  static constexpr int A_OFF = 0;
+  static constexpr int B_OFF = T::BM * kSliceBytes;
+  static constexpr int SA_OFF = B_OFF + T::BN * kSliceBytes;
+  static constexpr int SB_OFF = SA_OFF + SA_INSTR * 256;
+  static constexpr int RI_OFF = SB_OFF + SB_INSTR * 256;
+  static constexpr int C_OFF = RI_OFF + RI_INSTR * 256;
+  static constexpr int DUMMY_OFF = C_OFF + C_INSTR * 1024;
+  static constexpr int STAGE = DUMMY_OFF + (HAS_DUMMY ? 256 : 0);
+  static constexpr int PIPE = T::S * STAGE;
+
+  // Stores per wave per finished tile (each a 16-byte buffer store).
+  static constexpr int STORES = VAR == kKGrouped ? T::MJ * T::NI : T::MJ * (T::NI / 2);
+  static_assert(PER_WAVE * (T::S - 1) + (T::S - 1) * STORES <= 63, "vmcnt range");
+  static_assert(!ACC || (T::BN * 4 <= 1024 && 1024 % (T::BN * 4) == 0 && C_ROW_CHUNKS <= 64),
+                "accumulation tile staging: whole rows per copy");
+  static_assert(!(ACC && VAR != kKGrouped), "accumulation is K-grouped only");
+};
+
 template <class T, int VAR>
-__device__ __forceinline__ void sched_init(Sched<T, VAR>& S, const Params& p) {
+__device__ __forceinline__ void sched_init(Sched<T, VAR>& S, const Params& p, int* s_tmp,
+                                           int* s_flag) {
   const int tid = threadIdx.x;
   S.ntn = (p.N + T::BN - 1) / T::BN;
   if constexpr (VAR == kMasked) {
@@ -52,35 +112,37 @@ __device__ __forceinline__ void sched_init(Sched<T, VAR>& S, const Params& p) {
       S.s_a[g] = ((c + T::BM - 1) / T::BM) * S.ntn;
     }
     __syncthreads();
-    S.total = block_exclusive_scan(S.s_a, p.G, S.s_tmp);
+    S.total = block_exclusive_scan(S.s_a, p.G, s_tmp);
   } else if constexpr (VAR == kContig) {
+    // s_flag (transient, inside the pipeline stages) holds the block flags and then
+    // their prefix; valid blocks are packed into s_b in block order.
     const int nb = (p.rows + kContigBlock - 1) / kContigBlock;
     for (int b = tid; b < nb; b += kThreads) {
-      int e = p.meta[(long)b * kContigBlock];
-      bool ok = e >= 0 && e < p.G;
-      S.s_b[b] = ok ? e : -1;
-      S.s_a[b] = ok ? 1 : 0;
+      const int e = p.meta[(long)b * kContigBlock];
+      s_flag[b] = (e >= 0 && e < p.G) ? 1 : 0;
     }
     __syncthreads();
-    int nvalid = block_exclusive_scan(S.s_a, nb, S.s_tmp);
-    for (int b = tid; b < nb; b += kThreads)
-      if (S.s_b[b] >= 0) S.s_c[S.s_a[b]] = b;
+    const int nvalid = block_exclusive_scan(s_flag, nb, s_tmp);
+    for (int b = tid; b < nb; b += kThreads) {
+      const int e = p.meta[(long)b * kContigBlock];
+      if (e >= 0 && e < p.G) S.s_b[s_flag[b]] = (b << 12) | e;
+    }
     __syncthreads();
     S.total = nvalid * (kContigBlock / T::BM) * S.ntn;
   } else {
     S.mtn = (p.rows + T::BM - 1) / T::BM;
     for (int g = tid; g < p.G; g += kThreads) {
-      int k = p.meta[g];
+      const int k = p.meta[g];
       S.s_b[g] = k;
       S.s_a[g] = k > 0 ? k : 0;
     }
     __syncthreads();
-    block_exclusive_scan(S.s_a, p.G, S.s_tmp);
+    block_exclusive_scan(S.s_a, p.G, s_tmp);
     for (int g = tid; g < p.G; g += kThreads) {
       const int k = S.s_b[g];
       const int pe = S.s_a[g];
-      bool usable = k >= 0 && (k % p.k_granule) == 0 && (pe % p.k_granule) == 0 &&
-                    (long)pe + k <= (long)p.K;
+      const bool usable = k >= 0 && (k % p.k_granule) == 0 && (pe % p.k_granule) == 0 &&
+                          (long)pe + k <= (long)p.K;
       S.s_b[g] = usable ? k : -1;
     }
     __syncthreads();
@@ -92,28 +154,24 @@ __device__ __forceinline__ void sched_init(Sched<T, VAR>& S, const Params& p) {
 // grid size. Workgroups are dispatched to the 8 XCDs round-robin (block b runs on XCD
 // b % 8); each XCD gets a contiguous range of logical tiles per round so that
 // neighbouring tiles (same expert, same weight panel) share that XCD's L2.
-__device__ __forceinline__ long logical_tile(int it) {
+__device__ __forceinline__ long first_tile() {
   const int grid = gridDim.x, b = blockIdx.x;
-  if (grid % kXcds != 0) return (long)it * grid + b;
+  if (grid % kXcds != 0) return b;
   const int per = grid / kXcds;
-  return (long)it * grid + (long)(b % kXcds) * per + b / kXcds;
+  return (long)(b % kXcds) * per + b / kXcds;
 }
 
+// Decodes logical tile L; tiles with nothing to do are skipped by advancing L in steps
+// of the grid size, and L is left at the tile returned.
 template <class T, int VAR, int DT, int GRAN>
 __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Params& p, long& L) {
-  // Decodes logical tile L; tiles with nothing to do are skipped by advancing L in
-  // steps of the grid size (the same workgroup's later tiles), and L is left at the
-  // tile returned.
-  TileCtx t;
-  t.valid = 0;
+  TileCtx t = {};  // valid == 0, null bases: an idle cursor copies nothing
   constexpr int esz = DT == kFP8 ? 1 : 2;
-  const int Kd = p.K;  // masked/contiguous K (elements)
   if constexpr (VAR == kMasked) {
-    while (L < S.total) {
-      // largest g with prefix[g] <= L
-      int lo = 0, hi = p.G - 1;
+    if (L < S.total) {
+      int lo = 0, hi = p.G - 1;  // largest g with prefix[g] <= L
       while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
+        const int mid = (lo + hi + 1) >> 1;
         if (S.s_a[mid] <= L) lo = mid; else hi = mid - 1;
       }
       const int g = lo;
@@ -121,29 +179,32 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       const int mt_g = (c + T::BM - 1) / T::BM;
       const int local = (int)(L - S.s_a[g]);
       const int nt = local / mt_g, mt = local % mt_g;
+      const int Kb = p.K * esz;
+      const int KB = p.K / 128;
       t.valid = 1;
       t.g = g;
       t.m0 = mt * T::BM;
       t.n0 = nt * T::BN;
-      t.k_bytes = Kd * esz;
-      t.nk = (t.k_bytes + kSliceBytes - 1) / kSliceBytes;
+      t.k_bytes = Kb;
+      t.nk = (Kb + kSliceBytes - 1) / kSliceBytes;
       t.a_lim = c;
       t.row_end = c;
-      t.a_off = (long)g * p.rows * t.k_bytes;
-      t.b_off = (long)g * p.N * t.k_bytes;
-      t.lda = t.ldb = t.k_bytes;
-      const int KB = Kd / 128;
+      t.a_base = p.A + (long)g * p.rows * Kb;
+      t.a_bytes = (uint32_t)((long)p.rows * Kb);
+      t.b_base = p.B + (long)g * p.N * Kb;
+      t.b_bytes = (uint32_t)((long)p.N * Kb);
+      t.lda = t.ldb = Kb;
       t.sfa_off = (long)g * KB * p.rows;
       t.sfa_ld = p.rows;
       if constexpr (GRAN == kSfbBlock) {
         t.sfb_off = (long)g * ((p.N + 127) / 128) * KB;
-        t.sfb_ld = 1;  // consecutive scale groups of one block are adjacent
+        t.sfb_ld = KB;  // distance between consecutive 128-row blocks
       } else {
         t.sfb_off = (long)g * KB * p.N;
         t.sfb_ld = p.N;
       }
-      t.d_row0 = (long)g * p.rows * p.N;
-      break;
+      t.d_base = reinterpret_cast<uint8_t*>(p.D) + (long)g * p.rows * p.N * 2;
+      t.d_bytes = (uint32_t)((long)p.rows * p.N * 2);
     }
   } else if constexpr (VAR == kContig) {
     constexpr int SUB = kContigBlock / T::BM;
@@ -151,35 +212,38 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       const int nt = (int)(L % S.ntn);
       const long rest = L / S.ntn;
       const int sub = (int)(rest % SUB);
-      const int vb = (int)(rest / SUB);
-      const int blk = S.s_c[vb];
-      const int e = S.s_b[blk];
+      const int packed = S.s_b[rest / SUB];
+      const int blk = packed >> 12, e = packed & 0xfff;
       const int m0 = blk * kContigBlock + sub * T::BM;
       // A sub-tile that starts on padding is padding throughout (valid rows come first
       // in a block); skip it without loading anything.
-      if (m0 >= p.rows || (sub > 0 && p.meta[m0] != e)) { L += gridDim.x; continue; }
+      if (m0 >= p.rows || (SUB > 1 && sub > 0 && p.meta[m0] != e)) { L += gridDim.x; continue; }
+      const int Kb = p.K * esz;
+      const int KB = p.K / 128;
       t.valid = 1;
       t.g = e;
       t.m0 = m0;
       t.n0 = nt * T::BN;
-      t.k_bytes = Kd * esz;
-      t.nk = (t.k_bytes + kSliceBytes - 1) / kSliceBytes;
+      t.k_bytes = Kb;
+      t.nk = (Kb + kSliceBytes - 1) / kSliceBytes;
       t.a_lim = p.rows;
       t.row_end = p.rows;
-      t.a_off = 0;
-      t.b_off = (long)e * p.N * t.k_bytes;
-      t.lda = t.ldb = t.k_bytes;
-      const int KB = Kd / 128;
+      t.a_base = p.A;
+      t.a_bytes = (uint32_t)((long)p.rows * Kb);
+      t.b_base = p.B + (long)e * p.N * Kb;
+      t.b_bytes = (uint32_t)((long)p.N * Kb);
+      t.lda = t.ldb = Kb;
       t.sfa_off = 0;
       t.sfa_ld = p.rows;
       if constexpr (GRAN == kSfbBlock) {
         t.sfb_off = (long)e * ((p.N + 127) / 128) * KB;
-        t.sfb_ld = 1;
+        t.sfb_ld = KB;
       } else {
         t.sfb_off = (long)e * KB * p.N;
         t.sfb_ld = p.N;
       }
-      t.d_row0 = 0;
+      t.d_base = reinterpret_cast<uint8_t*>(p.D);
+      t.d_bytes = (uint32_t)((long)p.rows * p.N * 2);
       break;
     }
   } else {
@@ -199,14 +263,17 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       t.nk = t.k_bytes > 0 ? (t.k_bytes + kSliceBytes - 1) / kSliceBytes : 1;
       t.a_lim = p.rows;
       t.row_end = p.rows;
-      t.a_off = (long)p.rows * pe * esz;
-      t.b_off = (long)p.N * pe * esz;
-      t.lda = t.ldb = t.k_bytes;
+      t.a_base = p.A + (long)p.rows * pe * esz;
+      t.a_bytes = (uint32_t)((long)p.rows * k * esz);
+      t.b_base = p.B + (long)p.N * pe * esz;
+      t.b_bytes = (uint32_t)((long)p.N * k * esz);
+      t.lda = t.ldb = k * esz;
       t.sfa_off = (pe / 128) * p.rows;
       t.sfa_ld = p.rows;
       t.sfb_off = (pe / 128) * p.N;
       t.sfb_ld = p.N;
-      t.d_row0 = (long)e * p.rows * p.N;
+      t.d_base = reinterpret_cast<uint8_t*>(p.D) + (long)e * p.rows * p.N * 4;
+      t.d_bytes = (uint32_t)((long)p.rows * p.N * 4);
       break;
     }
   }
@@ -215,159 +282,209 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
 
 // ----------------------------------------------------------------------------- kernel
 
-template <class T, int VAR, int DT, int SF, int GRAN>
-struct Layout {
-  static constexpr bool FP8 = DT == kFP8;
-  static constexpr int A_BYTES = T::BM * kSliceBytes;
-  static constexpr int B_BYTES = T::BN * kSliceBytes;
-  static constexpr int SA_N = FP8 ? T::BM : 0;
-  static constexpr int SB_N = FP8 ? (GRAN == kSfbChannel ? T::BN : (T::BN + 127) / 128) : 0;
-  static constexpr int SA_OFF = A_BYTES + B_BYTES;
-  static constexpr int SB_OFF = SA_OFF + SA_N * 4;
-  static constexpr int STAGE = ((SB_OFF + SB_N * 4) + 15) / 16 * 16;
-  static constexpr int PIPE = 2 * STAGE;
-};
-
-template <class T, int VAR, int DT, int SF, int GRAN>
+template <class T, int VAR, int DT, int SF, int GRAN, bool ACC>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
-  using Lay = Layout<T, VAR, DT, SF, GRAN>;
+  using Lay = Layout<T, VAR, DT, SF, GRAN, ACC>;
   constexpr bool FP8 = Lay::FP8;
-  constexpr int NI = T::NI, MJ = T::MJ;
+  constexpr int NI = T::NI, MJ = T::MJ, S = T::S;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   const int wave_m = wave / T::WN, wave_n = wave % T::WN;
   const int wm0 = wave_m * T::WTM, wn0 = wave_n * T::WTN;
 
-  // ---- scheduler state in LDS after the two pipeline stages
-  Sched<T, VAR> S;
+  // ---- scheduler (its scan scratch lies in the pipeline stages, unused until the
+  // first copy is issued)
+  Sched<T, VAR> Sd;
   {
     int* base = reinterpret_cast<int*>(smem + Lay::PIPE);
-    S.s_tmp = base;
-    base += kThreads;
     const int n = (VAR == kContig) ? (p.rows + kContigBlock - 1) / kContigBlock : p.G;
-    S.s_a = base;
-    S.s_b = base + n;
-    S.s_c = base + 2 * n;
+    Sd.s_a = base;
+    Sd.s_b = base + (VAR == kContig ? 0 : n);
+    int* s_tmp = reinterpret_cast<int*>(smem);
+    int* s_flag = s_tmp + kThreads;
+    sched_init<T, VAR>(Sd, p, s_tmp, s_flag);
   }
-  sched_init<T, VAR>(S, p);
+  const uint32_t lds0 = lds_addr(smem);
+  const int grid = gridDim.x;
+
+  v4i rs_sfa = FP8 ? make_rsrc(p.SFA, p.sfa_bytes) : v4i{0, 0, 0, 0};
+  v4i rs_sfb = FP8 ? make_rsrc(p.SFB, p.sfb_bytes) : v4i{0, 0, 0, 0};
+  v4i rs_meta = make_rsrc(p.meta, p.meta_bytes);
+  pin_sgpr(rs_sfa);
+  pin_sgpr(rs_sfb);
+  pin_sgpr(rs_meta);
+
+  // ---- the issue cursor's per-tile copy state: resource descriptors and per-lane
+  // byte offsets of every operand-row copy slot (kOOB for rows outside the tile's
+  // valid range); a slice only adds its K offset.
+  struct Issue {
+    TileCtx t;
+    v4i rs_a, rs_b, rs_d;
+    uint32_t vab[Lay::U_AB];
+    uint32_t vc[Lay::U_C > 0 ? Lay::U_C : 1];
+  };
+  // Logical 16-byte chunk this lane copies: the LDS row of every copy is 8q + lane / 8
+  // (so its low 3 bits are lane / 8) and the chunk is XOR-swizzled with them.
+  const int c16 = ((lane & 7) ^ (lane >> 3)) << 4;
+  auto prepare = [&](Issue& I) {
+    const TileCtx& t = I.t;
+    I.rs_a = make_rsrc(t.a_base, t.a_bytes);
+    I.rs_b = make_rsrc(t.b_base, t.b_bytes);
+    I.rs_d = make_rsrc(t.d_base, t.d_bytes);
+    pin_sgpr(I.rs_a);
+    pin_sgpr(I.rs_b);
+    pin_sgpr(I.rs_d);
+#pragma unroll
+    for (int u = 0; u < Lay::U_AB; ++u) {
+      const int R = 8 * (4 * u + wave) + (lane >> 3);
+      if (u < Lay::U_A) {
+        const int m = t.m0 + R;
+        I.vab[u] = (t.valid && m < t.a_lim) ? (uint32_t)(m * t.lda + c16) : kOOB;
+      } else {
+        const int n = t.n0 + weight_row_of_lds<T>(R - T::BM);
+        I.vab[u] = (t.valid && n < p.N) ? (uint32_t)(n * t.ldb + c16) : kOOB;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < Lay::U_C; ++u) {
+      constexpr int ROWS_PER = 1024 / (T::BN * 4);
+      const int r = (4 * u + wave) * ROWS_PER + lane / Lay::C_ROW_CHUNKS;
+      const int pc = lane % Lay::C_ROW_CHUNKS;
+      const int c = pc ^ (r % Lay::C_ROW_CHUNKS);
+      const int m = t.m0 + r, n = t.n0 + 4 * c;
+      I.vc[u] = (t.valid && m < p.rows && n + 4 <= p.N) ? (uint32_t)(((long)m * p.N + n) * 4) : kOOB;
+    }
+  };
+
+  // ---- copies of one item (tile I.t, slice s) into stage `stg`; an idle cursor copies
+  // zeros so the instruction count never changes.
+  auto issue = [&](const Issue& I, int s, int stg) {
+    const TileCtx& t = I.t;
+    const uint32_t st = lds0 + stg * Lay::STAGE;
+    const int kb0 = s * kSliceBytes;
+    const bool full = kb0 + kSliceBytes <= t.k_bytes;  // no K tail inside this slice
+    const bool k_any = t.k_bytes > 0;
+    dma_fence();
+#pragma unroll
+    for (int u = 0; u < Lay::U_AB; ++u) {
+      uint32_t voff = I.vab[u] + kb0;
+      if (!full && kb0 + c16 + 16 > t.k_bytes) voff = kOOB;
+      dma_x4(st + Lay::A_OFF + 1024 * (4 * u + wave), u < Lay::U_A ? I.rs_a : I.rs_b, voff);
+    }
+#pragma unroll
+    for (int us = 0; us < Lay::U_SM; ++us) {
+      const int e = 4 * us + wave;  // small-copy index dealt to this wave (uniform)
+      if (e < Lay::SA_INSTR) {
+        const int l = 64 * e + lane;
+        const long o = t.sfa_off + (long)s * t.sfa_ld + t.m0;
+        uint32_t voff = kOOB;
+        if constexpr (SF == kSfF32) {
+          if (t.valid && k_any && l < T::BM) voff = (uint32_t)((o + l) * 4);
+        } else {
+          if (t.valid && k_any && l < Lay::SA_LANES) voff = (uint32_t)((o & ~3L) + 4 * l);
+        }
+        dma_x1(st + Lay::SA_OFF + 256 * e, rs_sfa, voff);
+      } else if (e < Lay::SA_INSTR + Lay::SB_INSTR) {
+        const int j = e - Lay::SA_INSTR;
+        const int l = 64 * j + lane;
+        uint32_t voff = kOOB;
+        if constexpr (GRAN == kSfbChannel) {
+          const long o = t.sfb_off + (long)s * t.sfb_ld + t.n0;
+          if constexpr (SF == kSfF32) {
+            if (t.valid && k_any && l < T::BN) voff = (uint32_t)((o + l) * 4);
+          } else {
+            if (t.valid && k_any && l < Lay::SB_LANES) voff = (uint32_t)((o & ~3L) + 4 * l);
+          }
+        } else {
+          const int nb = t.n0 / 128 + l;
+          const long o = t.sfb_off + (long)nb * t.sfb_ld + s;
+          if (t.valid && k_any && l < Lay::SBN_BLOCK && nb * 128 < p.N)
+            voff = SF == kSfF32 ? (uint32_t)(o * 4) : (uint32_t)(o & ~3L);
+        }
+        dma_x1(st + Lay::SB_OFF + 256 * j, rs_sfb, voff);
+      } else if (e < Lay::SMALL) {
+        const int j = e - Lay::SA_INSTR - Lay::SB_INSTR;
+        const int l = 64 * j + lane;
+        const int m = t.m0 + l;
+        dma_x1(st + Lay::RI_OFF + 256 * j, rs_meta,
+               (t.valid && l < T::BM && m < p.rows) ? (uint32_t)(m * 4) : kOOB);
+      } else {
+        dma_x1(st + Lay::DUMMY_OFF, rs_meta, kOOB);  // keeps the per-wave count uniform
+      }
+    }
+    // the accumulation input of a tile is needed by the epilogue of its last slice
+    const bool last = s == t.nk - 1;
+#pragma unroll
+    for (int u = 0; u < Lay::U_C; ++u)
+      dma_x4(st + Lay::C_OFF + 1024 * (4 * u + wave), I.rs_d, last ? I.vc[u] : kOOB);
+  };
 
   // ---- per-lane constant LDS offsets of the MFMA fragments (XOR swizzle folded in)
   const int x_lo = ((lg) ^ (lr & 7)) << 4;
   const int x_hi = ((lg + 4) ^ (lr & 7)) << 4;
-  int a_row_off[NI];  // weight fragment rows (first MFMA operand)
-  int b_row_off[MJ];  // activation fragment rows (second MFMA operand)
-#pragma unroll
-  for (int i = 0; i < NI; ++i) a_row_off[i] = Lay::A_BYTES + (wn0 + 16 * i + lr) * kSliceBytes;
-#pragma unroll
-  for (int j = 0; j < MJ; ++j) b_row_off[j] = (wm0 + 16 * j + lr) * kSliceBytes;
 
   v4f acc[NI][MJ];
-  v4i stage_regs[T::CH_PER_THREAD];
-  float sa_reg = 0.f, sb_reg = 0.f;
 
-  // Issue the global loads of slice `s` of tile `t` into registers.
-  auto load_slice = [&](const TileCtx& t, int s) {
-    const int kb0 = s * kSliceBytes;
-#pragma unroll
-    for (int u = 0; u < T::CH_PER_THREAD; ++u) {
-      const int q = tid + u * kThreads;
-      v4i v = {0, 0, 0, 0};
-      if (q < T::CHUNKS) {
-        const int row = q >> 3, c = q & 7;
-        const int kb = kb0 + c * 16;
-        const bool k_ok = kb + 16 <= t.k_bytes;
-        if (row < T::BM) {
-          const int m = t.m0 + row;
-          if (k_ok && m < t.a_lim)
-            v = *reinterpret_cast<const v4i*>(p.A + t.a_off + (long)m * t.lda + kb);
-        } else {
-          const int n = t.n0 + row - T::BM;
-          if (k_ok && n < p.N)
-            v = *reinterpret_cast<const v4i*>(p.B + t.b_off + (long)n * t.ldb + kb);
-        }
-      }
-      stage_regs[u] = v;
-    }
+  // MFMA work of one slice held in stage `stg`.
+  auto compute = [&](const TileCtx& t, int s, int stg) {
+    const uint8_t* st = smem + stg * Lay::STAGE;
     if constexpr (FP8) {
-      const bool k_ok = t.k_bytes > 0;
-      if (tid < T::BM) {
-        const int m = t.m0 + tid;
-        sa_reg = (k_ok && m < t.a_lim)
-                     ? load_scale<SF>(p.SFA, t.sfa_off + (long)s * t.sfa_ld + m) : 0.f;
-      }
-      if (tid < Lay::SB_N) {
-        if constexpr (GRAN == kSfbChannel) {
-          const int n = t.n0 + tid;
-          sb_reg = (k_ok && n < p.N)
-                       ? load_scale<SF>(p.SFB, t.sfb_off + (long)s * t.sfb_ld + n) : 0.f;
-        } else {
-          const int nb = t.n0 / 128 + tid;
-          const int KB = p.K / 128;
-          sb_reg = (k_ok && nb * 128 < p.N)
-                       ? load_scale<SF>(p.SFB, t.sfb_off + (long)nb * KB + s) : 0.f;
-        }
-      }
-    }
-  };
-
-  // Write the staged registers into LDS stage `buf`.
-  auto store_slice = [&](int buf) {
-    uint8_t* st = smem + buf * Lay::STAGE;
-#pragma unroll
-    for (int u = 0; u < T::CH_PER_THREAD; ++u) {
-      const int q = tid + u * kThreads;
-      if (q < T::CHUNKS) {
-        const int row = q >> 3, c = q & 7;
-        int off;
-        if (row < T::BM) off = swz(row, c);
-        else off = Lay::A_BYTES + swz(weight_lds_row<T>(row - T::BM), c);
-        *reinterpret_cast<v4i*>(st + off) = stage_regs[u];
-      }
-    }
-    if constexpr (FP8) {
-      float* sA = reinterpret_cast<float*>(st + Lay::SA_OFF);
-      float* sB = reinterpret_cast<float*>(st + Lay::SB_OFF);
-      if (tid < T::BM) sA[tid] = sa_reg;
-      if (tid < Lay::SB_N) sB[tid] = sb_reg;
-    }
-  };
-
-  // MFMA work of one slice held in LDS stage `buf`.
-  auto compute_slice = [&](int buf) {
-    const uint8_t* st = smem + buf * Lay::STAGE;
-    if constexpr (FP8) {
-      const float* sA = reinterpret_cast<const float*>(st + Lay::SA_OFF);
-      const float* sB = reinterpret_cast<const float*>(st + Lay::SB_OFF);
       v8i bfr[MJ];
       float sa[MJ];
+      const long oa = t.sfa_off + (long)s * t.sfa_ld + t.m0;
 #pragma unroll
       for (int j = 0; j < MJ; ++j) {
-        v4i lo = *reinterpret_cast<const v4i*>(st + b_row_off[j] + x_lo);
-        v4i hi = *reinterpret_cast<const v4i*>(st + b_row_off[j] + x_hi);
+        const int row = wm0 + 16 * j + lr;
+        const uint8_t* rp = st + Lay::A_OFF + row * kSliceBytes;
+        const v4i lo = *reinterpret_cast<const v4i*>(rp + x_lo);
+        const v4i hi = *reinterpret_cast<const v4i*>(rp + x_hi);
         bfr[j] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        sa[j] = sA[wm0 + 16 * j + lr];
+        if constexpr (SF == kSfF32)
+          sa[j] = reinterpret_cast<const float*>(st + Lay::SA_OFF)[row];
+        else
+          sa[j] = ue8m0_to_float(st[Lay::SA_OFF + (int)(oa & 3) + row]);
       }
       float sbw = 0.f;
-      if constexpr (GRAN == kSfbBlock) sbw = sB[wn0 / 128];
+      if constexpr (GRAN == kSfbBlock) {
+        const int lb = ((t.n0 & 127) + wn0) >> 7;
+        if constexpr (SF == kSfF32) {
+          sbw = reinterpret_cast<const float*>(st + Lay::SB_OFF)[lb];
+        } else {
+          const long ob = t.sfb_off + (long)(t.n0 / 128 + lb) * t.sfb_ld + s;
+          sbw = ue8m0_to_float(st[Lay::SB_OFF + 4 * lb + (int)(ob & 3)]);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        v4i lo = *reinterpret_cast<const v4i*>(st + a_row_off[i] + x_lo);
-        v4i hi = *reinterpret_cast<const v4i*>(st + a_row_off[i] + x_hi);
-        v8i afr = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        const uint8_t* rp = st + Lay::B_OFF + (wn0 + 16 * i + lr) * kSliceBytes;
+        const v4i lo = *reinterpret_cast<const v4i*>(rp + x_lo);
+        const v4i hi = *reinterpret_cast<const v4i*>(rp + x_hi);
+        const v8i afr = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         v4f sbv = {sbw, sbw, sbw, sbw};
-        if constexpr (GRAN == kSfbChannel)
-          sbv = *reinterpret_cast<const v4f*>(sB + wn0 + lg * 4 * NI + 4 * i);
+        if constexpr (GRAN == kSfbChannel) {
+          const int col = wn0 + lg * 4 * NI + 4 * i;
+          if constexpr (SF == kSfF32) {
+            sbv = *reinterpret_cast<const v4f*>(st + Lay::SB_OFF + 4 * col);
+          } else {
+            const long ob = t.sfb_off + (long)s * t.sfb_ld + t.n0;
+            const uint8_t* bp = st + Lay::SB_OFF + (int)(ob & 3) + col;
+            sbv = (v4f){ue8m0_to_float(bp[0]), ue8m0_to_float(bp[1]), ue8m0_to_float(bp[2]),
+                        ue8m0_to_float(bp[3])};
+          }
+        }
 #pragma unroll
         for (int j = 0; j < MJ; ++j) {
           const v4f zero = {0.f, 0.f, 0.f, 0.f};
           // format 0 = FP8 E4M3 for both operands; scale exponent 127 = 2^0
-          v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], zero, 0, 0,
-                                                                       0, 127, 0, 127);
+          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], zero,
+                                                                           0, 0, 0, 127, 0, 127);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(part[r], sa[j] * sbv[r], acc[i][j][r]);
+          for (int r = 0; r < 4; ++r)
+            acc[i][j][r] = __builtin_fmaf(part[r], sa[j] * sbv[r], acc[i][j][r]);
         }
       }
     } else {
@@ -376,10 +493,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
         const int xo = h ? x_hi : x_lo;
         v8bf bfr[MJ];
 #pragma unroll
-        for (int j = 0; j < MJ; ++j) bfr[j] = *reinterpret_cast<const v8bf*>(st + b_row_off[j] + xo);
+        for (int j = 0; j < MJ; ++j)
+          bfr[j] = *reinterpret_cast<const v8bf*>(st + Lay::A_OFF +
+                                                  (wm0 + 16 * j + lr) * kSliceBytes + xo);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-          v8bf afr = *reinterpret_cast<const v8bf*>(st + a_row_off[i] + xo);
+          const v8bf afr = *reinterpret_cast<const v8bf*>(st + Lay::B_OFF +
+                                                          (wn0 + 16 * i + lr) * kSliceBytes + xo);
 #pragma unroll
           for (int j = 0; j < MJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], acc[i][j], 0, 0, 0);
@@ -388,76 +508,95 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
     }
   };
 
-  // Row-masked store of the finished tile.
-  auto epilogue = [&](const TileCtx& t) {
+  // Row-masked stores of the finished tile: exactly Lay::STORES buffer stores per wave,
+  // lanes outside the valid rows / columns use an out-of-range offset.
+  auto epilogue = [&](const TileCtx& t, int stg) {
+    const uint8_t* st = smem + stg * Lay::STAGE;
+    const v4i rs_d = make_rsrc(t.d_base, t.d_bytes);
+    const int nl0 = wn0 + lg * 4 * NI;  // tile-local first column of this lane
+    const int n_start = t.n0 + nl0;
 #pragma unroll
     for (int j = 0; j < MJ; ++j) {
-      const int m = t.m0 + wm0 + 16 * j + lr;
+      const int rl = wm0 + 16 * j + lr;
+      const int m = t.m0 + rl;
       bool row_ok = m < t.row_end;
-      if constexpr (VAR == kContig) row_ok = row_ok && p.meta[m] == t.g;
-      const int n_start = t.n0 + wn0 + lg * 4 * NI;
-      if (!row_ok) continue;
+      if constexpr (VAR == kContig)
+        row_ok = row_ok && reinterpret_cast<const int*>(st + Lay::RI_OFF)[rl] == t.g;
       if constexpr (VAR == kKGrouped) {
-        float* drow = reinterpret_cast<float*>(p.D) + t.d_row0 + (long)m * p.N + n_start;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-          if (n_start + 4 * i + 4 <= p.N) {
-            v4f v = acc[i][j];
-            if (p.accumulate) v += *reinterpret_cast<const v4f*>(drow + 4 * i);
-            *reinterpret_cast<v4f*>(drow + 4 * i) = v;
+          v4f v = acc[i][j];
+          if constexpr (ACC) {
+            const int c = (nl0 + 4 * i) / 4;
+            const int pc = c ^ (rl % Lay::C_ROW_CHUNKS);
+            v += *reinterpret_cast<const v4f*>(st + Lay::C_OFF + rl * T::BN * 4 + pc * 16);
           }
+          const bool ok = row_ok && n_start + 4 * i + 4 <= p.N;
+          const uint32_t voff = ok ? (uint32_t)(((long)m * p.N + n_start + 4 * i) * 4) : kOOB;
+          store_b128(rs_d, voff, (v4i){__float_as_int(v[0]), __float_as_int(v[1]),
+                                       __float_as_int(v[2]), __float_as_int(v[3])});
         }
       } else {
-        uint16_t* drow = reinterpret_cast<uint16_t*>(p.D) + t.d_row0 + (long)m * p.N + n_start;
 #pragma unroll
         for (int h = 0; h < NI / 2; ++h) {
-          if (n_start + 8 * h + 8 <= p.N) {
-            const v4f x = acc[2 * h][j], y = acc[2 * h + 1][j];
-            v4i w = {(int)pack_bf16x2(x[0], x[1]), (int)pack_bf16x2(x[2], x[3]),
-                     (int)pack_bf16x2(y[0], y[1]), (int)pack_bf16x2(y[2], y[3])};
-            *reinterpret_cast<v4i*>(drow + 8 * h) = w;
-          }
+          const v4f x = acc[2 * h][j], y = acc[2 * h + 1][j];
+          const v4i w = {(int)pack_bf16x2(x[0], x[1]), (int)pack_bf16x2(x[2], x[3]),
+                         (int)pack_bf16x2(y[0], y[1]), (int)pack_bf16x2(y[2], y[3])};
+          const bool ok = row_ok && n_start + 8 * h + 8 <= p.N;
+          const uint32_t voff = ok ? (uint32_t)(((long)m * p.N + n_start + 8 * h) * 2) : kOOB;
+          store_b128(rs_d, voff, w);
         }
       }
     }
   };
 
-  // ---- flat pipeline over (tile, slice) work items: the loads of the next item (which
-  // may belong to the next tile) are in flight while the current one computes.
-  const int grid = gridDim.x;
-  long L = logical_tile(0);
-  TileCtx cur = decode_tile<T, VAR, DT, GRAN>(S, p, L);
-  if (!cur.valid) return;
-  int s = 0;
-  load_slice(cur, 0);
-  store_slice(0);
-  __syncthreads();
-  int buf = 0;
-  while (true) {
-    TileCtx nxt = cur;
-    int ns = s + 1;
-    long Ln = L;
-    if (ns >= cur.nk) {
-      Ln = L + grid;
-      nxt = decode_tile<T, VAR, DT, GRAN>(S, p, Ln);
-      ns = 0;
+  // ---- the pipeline
+  long Li = first_tile();
+  Issue ic;  // issue cursor
+  ic.t = decode_tile<T, VAR, DT, GRAN>(Sd, p, Li);
+  long Lc = Li;
+  TileCtx tc = ic.t;  // compute cursor
+  if (!tc.valid) return;
+  int si = 0, sc = 0;
+  auto advance = [&](TileCtx& t, long& L, int& s) -> bool {
+    if (t.valid && ++s >= t.nk) {
+      L += grid;
+      t = decode_tile<T, VAR, DT, GRAN>(Sd, p, L);
+      s = 0;
+      return true;
     }
-    if (nxt.valid) load_slice(nxt, ns);
-    if (s == 0) {
+    return false;
+  };
+  __syncthreads();  // scheduler scratch in stage memory is dead from here on
+  prepare(ic);
+#pragma unroll
+  for (int k = 0; k < S - 1; ++k) {
+    issue(ic, si, k);
+    if (advance(ic.t, Li, si)) prepare(ic);
+  }
+  // whether each of the last S-1 iterations ran an epilogue (uniform), newest in bit 0;
+  // their stores are younger than the copies waited for below
+  unsigned epi_hist = 0;
+  int it = 0;
+  while (true) {
+    vm_wait_steps<Lay::PER_WAVE * (S - 2), Lay::STORES, S - 1>(__builtin_popcount(epi_hist));
+    lds_barrier();
+    const int stg = it % S;
+    issue(ic, si, (it + S - 1) % S);
+    if (advance(ic.t, Li, si)) prepare(ic);
+    if (sc == 0) {
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < MJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
     }
-    compute_slice(buf);
-    if (s == cur.nk - 1) epilogue(cur);
-    if (!nxt.valid) break;
-    store_slice(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    cur = nxt;
-    L = Ln;
-    s = ns;
+    compute(tc, sc, stg);
+    const bool epi = sc == tc.nk - 1;
+    if (epi) epilogue(tc, stg);
+    epi_hist = ((epi_hist << 1) | (epi ? 1u : 0u)) & ((1u << (S - 1)) - 1u);
+    advance(tc, Lc, sc);
+    if (!tc.valid) break;
+    ++it;
   }
 }
 
