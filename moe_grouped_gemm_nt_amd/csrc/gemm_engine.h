@@ -37,6 +37,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 enum Variant { kMasked = 0, kContig = 1, kKGrouped = 2 };
 enum DType { kBF16 = 0, kFP8 = 1 };
@@ -76,7 +77,10 @@ struct Tile {
   static_assert(WM * WN == 4, "four waves per workgroup");
   static_assert(S >= 2 && S <= 6, "pipeline depth");
   static constexpr int WTM = BM / WM, WTN = BN / WN;
+  // FP8 runs 16x16x128 MFMAs (MJ x NI subtiles per wave); BF16 runs 32x32x16 MFMAs
+  // (MJ2 x NI2 subtiles), the BF16 shape with the full matrix-core rate on gfx950.
   static constexpr int MJ = WTM / 16, NI = WTN / 16;
+  static constexpr int MJ2 = WTM / 32, NI2 = WTN / 32;
   static_assert(MJ >= 1 && NI >= 2 && WTM % 16 == 0 && WTN % 16 == 0, "16x16 subtiles");
   static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's n range stays in one 128-row block");
   static_assert((BM + BN) % 32 == 0 && BM % 8 == 0, "whole 8-row copies, 4 waves");
@@ -142,29 +146,26 @@ __device__ int block_exclusive_scan(int* buf, int n, int* s_tmp) {
   return total;
 }
 
-// LDS row (within the weight tile) that holds tile-local weight row n. A wave's WTN
-// rows are reordered so that MFMA subtile i reads 16 consecutive LDS rows while lane
-// group q's outputs cover the contiguous n range [q*4*NI, (q+1)*4*NI) of the wave.
-template <class T>
-__device__ __forceinline__ int weight_lds_row(int n) {
-  const int w = n / T::WTN, nl = n % T::WTN;
-  const int q = nl / (4 * T::NI), rem = nl % (4 * T::NI);
-  const int i = rem / 4, r = rem % 4;
-  return w * T::WTN + 16 * i + 4 * q + r;
-}
-
-// Byte offset of (row, 16-byte chunk c) in a tile of 128-byte rows, XOR-swizzled so
-// that 8 consecutive rows read at the same logical chunk hit 8 different bank groups.
-__device__ __forceinline__ int swz(int row, int c) {
-  return row * kSliceBytes + ((c ^ (row & 7)) << 4);
-}
-
-// Inverse of weight_lds_row: the tile-local weight row stored in LDS row R.
-template <class T>
+// Weight-row order inside LDS. The first MFMA operand is fed with weight rows in LDS
+// order; the rows are permuted so that each lane's outputs cover contiguous weight
+// columns, which makes the epilogue 16-byte row-contiguous stores.
+//
+// FP8 (16x16 outputs: lane group q holds MFMA rows 4q..4q+3): a wave's WTN rows are
+// stored so that subtile i reads 16 consecutive LDS rows while lane group q covers the
+// contiguous range [q*4*NI, (q+1)*4*NI) of the wave.
+// BF16 (32x32 outputs: lane group g = lane / 32 holds MFMA rows 8t + 4g + r, t, r in
+// 0..3): MFMA row i of subtile s is weight row 32 s + 16 ((i >> 2) & 1) + 4 (i >> 3) +
+// (i & 3), so lane group g covers 16 contiguous rows of each subtile.
+template <class T, bool BF16>
 __device__ __forceinline__ int weight_row_of_lds(int R) {
   const int w = R / T::WTN, rl = R % T::WTN;
-  const int i = rl / 16, q = (rl % 16) / 4, r = rl % 4;
-  return w * T::WTN + q * 4 * T::NI + 4 * i + r;
+  if constexpr (BF16) {
+    const int s = rl / 32, i = rl % 32;
+    return w * T::WTN + 32 * s + 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
+  } else {
+    const int i = rl / 16, q = (rl % 16) / 4, r = rl % 4;
+    return w * T::WTN + q * 4 * T::NI + 4 * i + r;
+  }
 }
 
 // ----------------------------------------------------------------------------- buffers

@@ -7,6 +7,7 @@
 // values change between replays.
 
 #include <mutex>
+#include <type_traits>
 #include <string>
 #include <unordered_map>
 
@@ -28,10 +29,11 @@ mgg_status fail(mgg_status s, const std::string& msg) {
 // small-M shapes keep MFMA work proportional to the valid rows and put more
 // workgroups on the weight stream when experts receive few tokens; all of them
 // produce bitwise-identical results.
-using TileS = Tile<32, 64, 2, 2, 4>;    // <= 32 rows per expert
-using TileM = Tile<64, 128, 2, 2, 3>;   // <= 64 rows
-using TileL = Tile<128, 256, 2, 2, 3>;  // larger experts
-using TileK = Tile<64, 64, 2, 2, 4>;    // K-grouped output tiles
+using TileS8 = Tile<32, 64, 2, 2, 4>;    // FP8, <= 32 rows per expert
+using TileS16 = Tile<32, 128, 1, 4, 4>;  // BF16 (32x32 subtiles), <= 32 rows per expert
+using TileM = Tile<64, 128, 2, 2, 3>;    // <= 64 rows
+using TileL = Tile<128, 256, 2, 2, 3>;   // larger experts
+using TileK = Tile<64, 64, 2, 2, 4>;     // K-grouped output tiles
 
 enum TileId { kTileS = 0, kTileM = 1, kTileL = 2 };
 
@@ -135,6 +137,7 @@ mgg_status launch_tile(TileId tile, const Params& p, hipStream_t s) {
   // The largest tile needs the most LDS; fall back to the middle one when the
   // scheduler table does not fit next to it.
   if (tile == kTileL && lds_bytes<TileL, VAR, DT, SF, GRAN, false>(p) > kLdsBytes) tile = kTileM;
+  using TileS = std::conditional_t<DT == kFP8, TileS8, TileS16>;
   switch (tile) {
     case kTileS: return launch<TileS, VAR, DT, SF, GRAN, false>(p, m_tiles<TileS, VAR>(p), s);
     case kTileM: return launch<TileM, VAR, DT, SF, GRAN, false>(p, m_tiles<TileM, VAR>(p), s);

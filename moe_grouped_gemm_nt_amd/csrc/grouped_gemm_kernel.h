@@ -92,7 +92,10 @@ struct Layout {
   static constexpr int PIPE = T::S * STAGE;
 
   // Stores per wave per finished tile (each a 16-byte buffer store).
-  static constexpr int STORES = VAR == kKGrouped ? T::MJ * T::NI : T::MJ * (T::NI / 2);
+  static constexpr int STORES =
+      FP8 ? (VAR == kKGrouped ? T::MJ * T::NI : T::MJ * (T::NI / 2))
+          : (VAR == kKGrouped ? T::MJ2 * T::NI2 * 4 : T::MJ2 * T::NI2 * 2);
+  static_assert(FP8 || (T::WTM % 32 == 0 && T::WTN % 32 == 0), "BF16 needs 32x32 subtiles");
   static_assert(PER_WAVE * (T::S - 1) + (T::S - 1) * STORES <= 63, "vmcnt range");
   static_assert(!ACC || (T::BN * 4 <= 1024 && 1024 % (T::BN * 4) == 0 && C_ROW_CHUNKS <= 64),
                 "accumulation tile staging: whole rows per copy");
@@ -345,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
         const int m = t.m0 + R;
         I.vab[u] = (t.valid && m < t.a_lim) ? (uint32_t)(m * t.lda + c16) : kOOB;
       } else {
-        const int n = t.n0 + weight_row_of_lds<T>(R - T::BM);
+        const int n = t.n0 + weight_row_of_lds<T, !FP8>(R - T::BM);
         I.vab[u] = (t.valid && n < p.N) ? (uint32_t)(n * t.ldb + c16) : kOOB;
       }
     }
@@ -427,7 +430,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   const int x_lo = ((lg) ^ (lr & 7)) << 4;
   const int x_hi = ((lg + 4) ^ (lr & 7)) << 4;
 
-  v4f acc[NI][MJ];
+  constexpr int NI2 = T::NI2, MJ2 = T::MJ2;
+  v4f acc[FP8 ? NI : 1][FP8 ? MJ : 1];     // FP8: 16x16 subtiles
+  v16f acc2[FP8 ? 1 : NI2][FP8 ? 1 : MJ2];  // BF16: 32x32 subtiles
 
   // MFMA work of one slice held in stage `stg`.
   auto compute = [&](const TileCtx& t, int s, int stg) {
@@ -488,21 +493,23 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
         }
       }
     } else {
+      // 32x32x16 MFMAs: MFMA h of the slice takes K elements 16h .. 16h + 15; lane group
+      // g = lane / 32 supplies elements 16h + 8g .. 16h + 8g + 7, the 16-byte chunk
+      // 2h + g of its row.
+      const int l32 = lane & 31, g2 = lane >> 5;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int xo = h ? x_hi : x_lo;
-        v8bf bfr[MJ];
+      for (int h = 0; h < 4; ++h) {
+        const int xo = ((2 * h + g2) ^ (l32 & 7)) << 4;
+        v8bf bfr[MJ2];
 #pragma unroll
-        for (int j = 0; j < MJ; ++j)
-          bfr[j] = *reinterpret_cast<const v8bf*>(st + Lay::A_OFF +
-                                                  (wm0 + 16 * j + lr) * kSliceBytes + xo);
+        for (int j = 0; j < MJ2; ++j)
+          bfr[j] = *reinterpret_cast<const v8bf*>(st + Lay::A_OFF + (wm0 + 32 * j + l32) * kSliceBytes + xo);
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const v8bf afr = *reinterpret_cast<const v8bf*>(st + Lay::B_OFF +
-                                                          (wn0 + 16 * i + lr) * kSliceBytes + xo);
+        for (int i = 0; i < NI2; ++i) {
+          const v8bf afr = *reinterpret_cast<const v8bf*>(st + Lay::B_OFF + (wn0 + 32 * i + l32) * kSliceBytes + xo);
 #pragma unroll
-          for (int j = 0; j < MJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < MJ2; ++j)
+            acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[j], acc2[i][j], 0, 0, 0);
         }
       }
     }
@@ -513,38 +520,84 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   auto epilogue = [&](const TileCtx& t, int stg) {
     const uint8_t* st = smem + stg * Lay::STAGE;
     const v4i rs_d = make_rsrc(t.d_base, t.d_bytes);
-    const int nl0 = wn0 + lg * 4 * NI;  // tile-local first column of this lane
-    const int n_start = t.n0 + nl0;
+    if constexpr (FP8) {
+      const int nl0 = wn0 + lg * 4 * NI;  // tile-local first column of this lane
+      const int n_start = t.n0 + nl0;
 #pragma unroll
-    for (int j = 0; j < MJ; ++j) {
-      const int rl = wm0 + 16 * j + lr;
-      const int m = t.m0 + rl;
-      bool row_ok = m < t.row_end;
-      if constexpr (VAR == kContig)
-        row_ok = row_ok && reinterpret_cast<const int*>(st + Lay::RI_OFF)[rl] == t.g;
-      if constexpr (VAR == kKGrouped) {
+      for (int j = 0; j < MJ; ++j) {
+        const int rl = wm0 + 16 * j + lr;
+        const int m = t.m0 + rl;
+        bool row_ok = m < t.row_end;
+        if constexpr (VAR == kContig)
+          row_ok = row_ok && reinterpret_cast<const int*>(st + Lay::RI_OFF)[rl] == t.g;
+        if constexpr (VAR == kKGrouped) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          v4f v = acc[i][j];
-          if constexpr (ACC) {
-            const int c = (nl0 + 4 * i) / 4;
-            const int pc = c ^ (rl % Lay::C_ROW_CHUNKS);
-            v += *reinterpret_cast<const v4f*>(st + Lay::C_OFF + rl * T::BN * 4 + pc * 16);
+          for (int i = 0; i < NI; ++i) {
+            v4f v = acc[i][j];
+            if constexpr (ACC) {
+              const int c = (nl0 + 4 * i) / 4;
+              const int pc = c ^ (rl % Lay::C_ROW_CHUNKS);
+              v += *reinterpret_cast<const v4f*>(st + Lay::C_OFF + rl * T::BN * 4 + pc * 16);
+            }
+            const bool ok = row_ok && n_start + 4 * i + 4 <= p.N;
+            const uint32_t voff = ok ? (uint32_t)(((long)m * p.N + n_start + 4 * i) * 4) : kOOB;
+            store_b128(rs_d, voff, (v4i){__float_as_int(v[0]), __float_as_int(v[1]),
+                                         __float_as_int(v[2]), __float_as_int(v[3])});
           }
-          const bool ok = row_ok && n_start + 4 * i + 4 <= p.N;
-          const uint32_t voff = ok ? (uint32_t)(((long)m * p.N + n_start + 4 * i) * 4) : kOOB;
-          store_b128(rs_d, voff, (v4i){__float_as_int(v[0]), __float_as_int(v[1]),
-                                       __float_as_int(v[2]), __float_as_int(v[3])});
-        }
-      } else {
+        } else {
 #pragma unroll
-        for (int h = 0; h < NI / 2; ++h) {
-          const v4f x = acc[2 * h][j], y = acc[2 * h + 1][j];
-          const v4i w = {(int)pack_bf16x2(x[0], x[1]), (int)pack_bf16x2(x[2], x[3]),
-                         (int)pack_bf16x2(y[0], y[1]), (int)pack_bf16x2(y[2], y[3])};
-          const bool ok = row_ok && n_start + 8 * h + 8 <= p.N;
-          const uint32_t voff = ok ? (uint32_t)(((long)m * p.N + n_start + 8 * h) * 2) : kOOB;
-          store_b128(rs_d, voff, w);
+          for (int h = 0; h < NI / 2; ++h) {
+            const v4f x = acc[2 * h][j], y = acc[2 * h + 1][j];
+            const v4i w = {(int)pack_bf16x2(x[0], x[1]), (int)pack_bf16x2(x[2], x[3]),
+                           (int)pack_bf16x2(y[0], y[1]), (int)pack_bf16x2(y[2], y[3])};
+            const bool ok = row_ok && n_start + 8 * h + 8 <= p.N;
+            const uint32_t voff = ok ? (uint32_t)(((long)m * p.N + n_start + 8 * h) * 2) : kOOB;
+            store_b128(rs_d, voff, w);
+          }
+        }
+      }
+    } else {
+      // 32x32 outputs: the lane holds column m = 32 j + lane % 32 and 16 contiguous
+      // weight columns 32 i + 16 (lane / 32) + r of each subtile (weight_row_of_lds).
+      const int l32 = lane & 31, g2 = lane >> 5;
+#pragma unroll
+      for (int j = 0; j < MJ2; ++j) {
+        const int rl = wm0 + 32 * j + l32;
+        const int m = t.m0 + rl;
+        bool row_ok = m < t.row_end;
+        if constexpr (VAR == kContig)
+          row_ok = row_ok && reinterpret_cast<const int*>(st + Lay::RI_OFF)[rl] == t.g;
+#pragma unroll
+        for (int i = 0; i < NI2; ++i) {
+          const int nl0 = wn0 + 32 * i + 16 * g2;
+          const int n_start = t.n0 + nl0;
+          const v16f v = acc2[i][j];
+          if constexpr (VAR == kKGrouped) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              v4f x = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+              if constexpr (ACC) {
+                const int c = nl0 / 4 + q;
+                const int pc = c ^ (rl % Lay::C_ROW_CHUNKS);
+                x += *reinterpret_cast<const v4f*>(st + Lay::C_OFF + rl * T::BN * 4 + pc * 16);
+              }
+              const bool ok = row_ok && n_start + 4 * q + 4 <= p.N;
+              const uint32_t voff = ok ? (uint32_t)(((long)m * p.N + n_start + 4 * q) * 4) : kOOB;
+              store_b128(rs_d, voff, (v4i){__float_as_int(x[0]), __float_as_int(x[1]),
+                                           __float_as_int(x[2]), __float_as_int(x[3])});
+            }
+          } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const v4i w = {(int)pack_bf16x2(v[8 * h + 0], v[8 * h + 1]),
+                             (int)pack_bf16x2(v[8 * h + 2], v[8 * h + 3]),
+                             (int)pack_bf16x2(v[8 * h + 4], v[8 * h + 5]),
+                             (int)pack_bf16x2(v[8 * h + 6], v[8 * h + 7])};
+              const bool ok = row_ok && n_start + 8 * h + 8 <= p.N;
+              const uint32_t voff = ok ? (uint32_t)(((long)m * p.N + n_start + 8 * h) * 2) : kOOB;
+              store_b128(rs_d, voff, w);
+            }
+          }
         }
       }
     }
@@ -585,10 +638,17 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
     issue(ic, si, (it + S - 1) % S);
     if (advance(ic.t, Li, si)) prepare(ic);
     if (sc == 0) {
+      if constexpr (FP8) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < MJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+          for (int j = 0; j < MJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+      } else {
+#pragma unroll
+        for (int i = 0; i < NI2; ++i)
+#pragma unroll
+          for (int j = 0; j < MJ2; ++j) acc2[i][j] = (v16f){};
+      }
     }
     compute(tc, sc, stg);
     const bool epi = sc == tc.nk - 1;
