@@ -23,12 +23,49 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}
 MALL_BYTES = 256 << 20
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "moe_grouped_gemm_nt_amd", "csrc")
+
+
+def kernel_source_digest() -> str:
+    """SHA-256 over the kernel sources (names and bytes, sorted), so that HBM counter
+    readings taken on one version of the kernel are never reported for another."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".h", ".hip")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the calibrated FETCH_SIZE / WRITE_SIZE readings stored in
+    profiles/<workload>_hbm_traffic.md, or None when there are none for the current
+    kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"^\s*-\s*([a-z_0-9-]+):\s*(\S+)", line)
+            if m:
+                fields[m.group(1)] = m.group(2)
+    if fields.get("kernel-source-sha256") != kernel_source_digest():
+        return None
+    try:
+        return int(fields["fetch_bytes_per_launch"]) + int(fields["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -42,6 +79,14 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--rotate", type=int, default=0,
                     help="output buffers to rotate over (0: enough to exceed the MALL)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="(no GPU) write profiles/<workload>_kernel_trace.md from the csv "
+                         "output of `rocprofv3 --kernel-trace --stats` of this script")
+    ap.add_argument("--summarize-traffic", nargs=4,
+                    metavar=("COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
+                    help="(no GPU) write profiles/<workload>_hbm_traffic.md from the csv "
+                         "output of four `rocprofv3 --pmc` runs: FETCH_SIZE and WRITE_SIZE of "
+                         "--workload copy_calibration, then of the workload")
     return ap.parse_args()
 
 
@@ -76,6 +121,9 @@ def algorithmic_bytes(p, opt) -> int:
 
 def main():
     args = parse()
+    if args.summarize_trace or args.summarize_traffic:
+        summarize(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the grouped GEMM shards by expert across GPUs with no exchange inside the "
@@ -160,7 +208,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(tflops, 1),
                 "peak": MFMA_PEAK_TFLOPS[p.dtype], "unit": "TFLOP/s",
                 "frac": round(tflops / MFMA_PEAK_TFLOPS[p.dtype], 4)}
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(args.workload)
     roof["algorithmic_bytes_per_launch"] = abytes
     roof["avg_launch_us"] = round(ms_step * 1e3, 3)
 
@@ -222,6 +270,99 @@ def copy_calibration(dev, args):
           flush=True)
 
 
+KERNEL_NAME = "grouped_gemm_kernel"
+COPY_KERNEL_NAME = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 256 << 20
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _counter_median(directory, kernel_sub):
+    import statistics
+    vals = [float(r["Counter_Value"]) for r in _csv_rows(directory, "counter_collection.csv")
+            if kernel_sub in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no {kernel_sub} dispatches in {directory}")
+    return statistics.median(vals), len(vals)
+
+
+def summarize(args):
+    """Turn rocprofv3 csv output into the short summaries kept under profiles/."""
+    out_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    w = args.workload
+    if args.summarize_trace:
+        d = args.summarize_trace
+        stats = [r for r in _csv_rows(d, "kernel_stats.csv") if KERNEL_NAME in r["Name"]]
+        trace = [r for r in _csv_rows(d, "kernel_trace.csv") if KERNEL_NAME in r["Kernel_Name"]]
+        if not stats:
+            raise SystemExit(f"no {KERNEL_NAME} in {d}")
+        lines = [f"# {KERNEL_NAME}: kernel trace, workload {w}", "",
+                 "Command (repository root, one MI355X):", "",
+                 f"    rocprofv3 --kernel-trace --stats -d {d} -o {w} --output-format csv "
+                 f"-- python -u bench.py --workload {w} --no-cpu-baseline", "",
+                 "Kernel statistics (`*_kernel_stats.csv`):", "",
+                 "| Kernel | Calls | Average (ns) | Min (ns) | Max (ns) | StdDev (ns) |",
+                 "|---|---|---|---|---|---|"]
+        for r in stats:
+            lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                         f"{r['MinNs']} | {r['MaxNs']} | {float(r['StdDev']):.0f} |")
+        if trace:
+            t = trace[-1]
+            gx = int(t.get("Grid_Size_X") or t.get("Grid_Size") or 0)
+            wx = int(t.get("Workgroup_Size_X") or t.get("Workgroup_Size") or 1)
+            lines += ["", f"Launch shape (`*_kernel_trace.csv`): {gx // wx} workgroups of {wx} "
+                      f"lanes; VGPR {t.get('VGPR_Count')}, AGPR {t.get('Accum_VGPR_Count')}, "
+                      f"SGPR {t.get('SGPR_Count')} (LDS is allocated dynamically, so the trace "
+                      f"lists {t.get('LDS_Block_Size')} B of static LDS)."]
+        lines += ["", f"kernel-source-sha256 of the profiled build: {kernel_source_digest()}", ""]
+        path = os.path.join(out_dir, f"{w}_kernel_trace.md")
+        with open(path, "w") as f:
+            f.write("\n".join(lines))
+        print(f"wrote {path}")
+    if args.summarize_traffic:
+        cf, cw, kf, kw = args.summarize_traffic
+        copy_f, _ = _counter_median(cf, COPY_KERNEL_NAME)
+        copy_w, _ = _counter_median(cw, COPY_KERNEL_NAME)
+        ker_f, nf = _counter_median(kf, KERNEL_NAME)
+        ker_w, nw = _counter_median(kw, KERNEL_NAME)
+        fac_f = COPY_BYTES / (copy_f * 1024.0)
+        fac_w = COPY_BYTES / (copy_w * 1024.0)
+        fetch = int(round(ker_f * 1024.0 * fac_f))
+        write = int(round(ker_w * 1024.0 * fac_w))
+        cmd = ("timeout -s KILL 120 rocprofv3 --pmc {c} -d {d} -o {o} --output-format csv -- "
+               "python -u bench.py --workload {w} --steps {s} --warmup 2{x}")
+        lines = [f"# {KERNEL_NAME}: HBM traffic, workload {w}", "",
+                 "Commands (repository root, one MI355X), one counter per run:", ""]
+        for c, d, ww, o, s, x in [("FETCH_SIZE", cf, "copy_calibration", "copy", 10, ""),
+                                  ("WRITE_SIZE", cw, "copy_calibration", "copy", 10, ""),
+                                  ("FETCH_SIZE", kf, w, "w", 20, " --no-cpu-baseline"),
+                                  ("WRITE_SIZE", kw, w, "w", 20, " --no-cpu-baseline")]:
+            lines.append("    " + cmd.format(c=c, d=d, o=o, w=ww, s=s, x=x))
+        lines += ["", "Calibration: the copy reads and writes exactly "
+                  f"{COPY_BYTES} B per launch; its median FETCH_SIZE is {copy_f:.1f} KiB and "
+                  f"WRITE_SIZE {copy_w:.1f} KiB, so the counters are scaled by "
+                  f"{fac_f:.4f} (fetch) and {fac_w:.4f} (write).", "",
+                  f"Kernel medians: FETCH_SIZE {ker_f:.1f} KiB over {nf} dispatches, "
+                  f"WRITE_SIZE {ker_w:.1f} KiB over {nw} dispatches.", "",
+                  "Values read by bench.py (bytes per launch, after scaling):", "",
+                  f"- kernel-source-sha256: {kernel_source_digest()}",
+                  f"- fetch_bytes_per_launch: {fetch}",
+                  f"- write_bytes_per_launch: {write}", ""]
+        path = os.path.join(out_dir, f"{w}_hbm_traffic.md")
+        with open(path, "w") as f:
+            f.write("\n".join(lines))
+        print(f"wrote {path}")
+
+
 def cpu_baseline(p, opt, flops, target_s):
     """The oracle, as it stands, on the host cores: a bounded sample of the same workload
     (whole experts, or a subset of experts for the large masked shapes)."""
@@ -278,7 +419,7 @@ def cpu_baseline(p, opt, flops, target_s):
         run()
         passes += 1
         t = time.perf_counter() - t0
-        if t >= target_s or passes >= 50:
+        if t >= target_s or passes >= 10000:
             break
     return {"value": round(unit_flops * passes / t / 1e12, 6), "unit": "TFLOPS",
             "cores": int(threads), "kind": "oracle",
