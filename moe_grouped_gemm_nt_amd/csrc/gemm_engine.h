@@ -1,20 +1,24 @@
 // gemm_engine.h - the gfx950 grouped NT GEMM engine shared by the masked, contiguous
 // and K-grouped entry points.
 //
-// One persistent kernel per call. Each workgroup (256 lanes = 4 wave64s):
+// One persistent kernel per call. Each workgroup (4 wave64s; 8 when an accumulation
+// input is read, see below):
 //   1. reads the device-side routing (masked counts, contiguous row indices, K-grouped
 //      token counts) into LDS and builds the tile prefix there, so nothing about the
 //      expert distribution is baked into the launch (a captured hipGraph replays
 //      correctly with new routing values);
 //   2. walks its share of the (expert, m-tile, n-tile) list with an XCD-aware order;
 //   3. per tile, streams 128-byte K slices of the activation rows and weight rows
-//      through double-buffered, XOR-swizzled LDS with coalesced 16-byte loads and
-//      feeds MFMA 16x16 instructions (FP8: 16x16x128 f8f6f4, one instruction per 128-K
-//      scale group; BF16: 16x16x32 bf16);
+//      through an S-stage ring of XOR-swizzled LDS buffers filled by direct global ->
+//      LDS copies, and feeds MFMAs (FP8: 16x16x128 f8f6f4, one instruction per 128-K
+//      scale group; BF16: 32x32x16 bf16);
 //   4. FP8 only: promotes each 128-K partial sum into the FP32 accumulator with the
 //      row scale times the weight scale (per-128-K promotion in registers);
 //   5. stores rows under a per-row mask: a tile never writes past its expert's valid
 //      rows, padding rows or another expert's rows.
+// With an accumulation input (K-grouped D = C + A B^T) four more waves own the
+// epilogue: they prefetch C tiles several tiles ahead straight into registers, add the
+// MFMA waves' results handed over through LDS, and store D.
 //
 // Operand roles. The MFMA's first operand is fed with WEIGHT rows (n) and its second
 // with ACTIVATION rows (m), so each lane ends up holding 4 consecutive n of one m; the
@@ -23,8 +27,8 @@
 //
 // K order. Inside one MFMA the K elements a lane supplies may be any fixed permutation
 // as long as both operands use the same one; lanes 16g..16g+15 supply the 16-byte K
-// chunks g and g+4 of each 128-byte slice. Across slices K ascends. The layout, the
-// instruction and the promotion formula do not depend on the tile shape, so every
+// chunks g and g+4 of each 128-byte slice (FP8). Across slices K ascends. The layout,
+// the instruction and the promotion formula do not depend on the tile shape, so every
 // tile configuration produces the same bits.
 #pragma once
 
@@ -44,7 +48,11 @@ enum DType { kBF16 = 0, kFP8 = 1 };
 enum SfFmt { kSfF32 = 0, kSfUE8M0 = 1 };
 enum SfbGran { kSfbBlock = 0, kSfbChannel = 1 };
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;     // the MFMA waves of a workgroup
+// Tiles of accumulation input in flight per epilogue wave. Deeper prefetch measured
+// slower on the K-grouped wgrad shape: the extra C loads queue in front of the MFMA
+// waves' operand copies in the CU's memory pipeline.
+constexpr int kCPrefetch = 2;
 constexpr int kSliceBytes = 128;  // K bytes per row per pipeline stage
 constexpr int kXcds = 8;          // MI355X: 8 accelerator dies, WGs dispatched round-robin
 constexpr int kContigBlock = 128; // rows per contiguous-layout alignment block
@@ -114,13 +122,14 @@ __device__ __forceinline__ float load_scale(const void* base, long idx) {
   }
 }
 
-// Exclusive scan of `n` ints held in LDS `buf` (in place), block-wide; returns the total.
-// Every thread of the block must call it; `s_tmp` needs 4 ints. Each thread sums a
-// contiguous chunk, waves scan their 64 partial sums with cross-lane shuffles, and the
-// four wave totals are combined through LDS (two barriers in all).
+// Exclusive scan of `n` ints held in LDS `buf` (in place), block-wide over NT threads;
+// returns the total. Every thread of the block must call it; `s_tmp` needs NT / 64
+// ints. Each thread sums a contiguous chunk, waves scan their 64 partial sums with
+// cross-lane shuffles, and the wave totals are combined through LDS (two barriers).
+template <int NT>
 __device__ int block_exclusive_scan(int* buf, int n, int* s_tmp) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = (n + kThreads - 1) / kThreads;
+  const int per = (n + NT - 1) / NT;
   const int lo = tid * per;
   const int hi = min(lo + per, n);
   int local = 0;
@@ -133,9 +142,12 @@ __device__ int block_exclusive_scan(int* buf, int n, int* s_tmp) {
   }
   if (lane == 63) s_tmp[wave] = incl;
   __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += s_tmp[w];
-  const int total = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    before += w < wave ? s_tmp[w] : 0;
+    total += s_tmp[w];
+  }
   int run = before + incl - local;  // exclusive prefix of this thread's chunk
   for (int i = lo; i < hi; ++i) {
     const int v = buf[i];
@@ -243,6 +255,14 @@ extern "C" __device__ void mgg_raw_buffer_store_v4i32(v4i vdata, v4i rsrc, int v
 
 __device__ __forceinline__ void store_b128(v4i rsrc, uint32_t voff, v4i v) {
   mgg_raw_buffer_store_v4i32(v, rsrc, (int)voff, 0, 0);
+}
+
+// The matching load into registers; the compiler tracks its completion like any load.
+extern "C" __device__ v4i mgg_raw_buffer_load_v4i32(v4i rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+
+__device__ __forceinline__ v4i load_b128(v4i rsrc, uint32_t voff) {
+  return mgg_raw_buffer_load_v4i32(rsrc, (int)voff, 0, 0);
 }
 
 }  // namespace mgg

@@ -33,7 +33,7 @@ using TileS8 = Tile<32, 64, 2, 2, 4>;    // FP8, <= 32 rows per expert
 using TileS16 = Tile<32, 128, 1, 4, 4>;  // BF16 (32x32 subtiles), <= 32 rows per expert
 using TileM = Tile<64, 128, 2, 2, 3>;    // <= 64 rows
 using TileL = Tile<128, 256, 2, 2, 3>;   // larger experts
-using TileK = Tile<64, 64, 2, 2, 4>;     // K-grouped output tiles
+using TileK = Tile<64, 128, 2, 2, 3>;    // K-grouped output tiles
 
 enum TileId { kTileS = 0, kTileM = 1, kTileL = 2 };
 
@@ -82,14 +82,15 @@ template <class T, int VAR, int DT, int SF, int GRAN, bool ACC>
 long lds_bytes(const Params& p) {
   long pers, trans;
   sched_bytes<VAR>(p, &pers, &trans);
-  const long pipe = Layout<T, VAR, DT, SF, GRAN, ACC>::PIPE;
-  if (trans > pipe) return 1L << 40;
-  return pipe + pers;
+  using Lay = Layout<T, VAR, DT, SF, GRAN, ACC>;
+  if (trans > Lay::PIPE) return 1L << 40;
+  return Lay::SCHED_OFF + pers;
 }
 
 template <class T, int VAR, int DT, int SF, int GRAN, bool ACC>
 mgg_status launch(const Params& p, long max_tiles, hipStream_t stream) {
   auto kern = grouped_gemm_kernel<T, VAR, DT, SF, GRAN, ACC>;
+  using Lay = Layout<T, VAR, DT, SF, GRAN, ACC>;
   const long lds = lds_bytes<T, VAR, DT, SF, GRAN, ACC>(p);
   if (lds > kLdsBytes)
     return fail(MGG_EUNSUPPORTED, "too many experts or row blocks for the LDS scheduler");
@@ -105,8 +106,8 @@ mgg_status launch(const Params& p, long max_tiles, hipStream_t stream) {
         return fail(MGG_EHIP, "hipFuncSetAttribute failed");
       // Residency at the pipeline's own footprint plus a typical scheduler table.
       int o = 0;
-      const size_t lds_typ = (size_t)Layout<T, VAR, DT, SF, GRAN, ACC>::PIPE + 4096;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, kThreads, lds_typ) !=
+      const size_t lds_typ = (size_t)Lay::SCHED_OFF + 4096;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, Lay::NT, lds_typ) !=
               hipSuccess || o < 1)
         o = 1;
       g_occ[(const void*)kern] = o;
@@ -119,7 +120,7 @@ mgg_status launch(const Params& p, long max_tiles, hipStream_t stream) {
   long grid = max_tiles < resident ? max_tiles : resident;
   if (grid >= kXcds) grid -= grid % kXcds;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), (size_t)lds, stream, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Lay::NT), (size_t)lds, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MGG_EHIP, std::string("kernel launch: ") + hipGetErrorString(e));
   return MGG_OK;

@@ -13,6 +13,14 @@
 // operations are younger than the copies of item i and waits for exactly those
 // (vmcnt counts in issue order). One barrier per item then makes every wave's copies
 // visible and guarantees the stage about to be refilled is no longer being read.
+//
+// Accumulating K-grouped calls (D = C + A B^T) add four epilogue waves. The MFMA waves
+// write each finished tile into one of two LDS exchange buffers instead of storing it;
+// the epilogue waves keep the C tiles of the next kCPrefetch tiles in flight in their
+// registers, and after the barrier that publishes a tile they add it to its C tile
+// and store D. Both wave groups walk the same tile sequence and execute the same
+// number of barriers (the MFMA waves one per item plus a final one, the epilogue waves
+// the same count arranged per tile), so the exchange needs no other synchronisation.
 #pragma once
 
 #include "gemm_engine.h"
@@ -67,18 +75,14 @@ struct Layout {
   static constexpr int SA_INSTR = cdiv(SA_LANES, 64);
   static constexpr int SB_INSTR = cdiv(SB_LANES, 64);
   static constexpr int RI_INSTR = VAR == kContig ? cdiv(T::BM, 64) : 0;
-  static constexpr int C_ROW_CHUNKS = T::BN / 4;  // 16-byte chunks per fp32 output row
-  static constexpr int C_INSTR = ACC ? T::BM * T::BN * 4 / 1024 : 0;
   // Copy slots per wave. Operand rows: slot u of wave w copies rows 8(4u + w) ..
   // 8(4u + w) + 7 of the [A; B] tile, so A and B slots are fixed per u (BM % 32 == 0).
   // Scale and row-index copies are few: they are dealt to the four waves ("small"
-  // slots, padded with a dummy copy). Accumulation-input copies take U_C whole slots.
+  // slots, padded with a dummy copy).
   static constexpr int U_A = T::BM / 32, U_B = T::BN / 32, U_AB = U_A + U_B;
   static constexpr int SMALL = SA_INSTR + SB_INSTR + RI_INSTR;
   static constexpr int U_SM = cdiv(SMALL, 4);
-  static_assert(C_INSTR % 4 == 0, "accumulation-input copies split evenly over 4 waves");
-  static constexpr int U_C = C_INSTR / 4;
-  static constexpr int PER_WAVE = U_AB + U_SM + U_C;  // copy instructions per wave per item
+  static constexpr int PER_WAVE = U_AB + U_SM;  // copy instructions per wave per item
   static constexpr bool HAS_DUMMY = U_SM * 4 > SMALL;
 
   static constexpr int A_OFF = 0;
@@ -86,47 +90,59 @@ struct Layout {
   static constexpr int SA_OFF = B_OFF + T::BN * kSliceBytes;
   static constexpr int SB_OFF = SA_OFF + SA_INSTR * 256;
   static constexpr int RI_OFF = SB_OFF + SB_INSTR * 256;
-  static constexpr int C_OFF = RI_OFF + RI_INSTR * 256;
-  static constexpr int DUMMY_OFF = C_OFF + C_INSTR * 1024;
+  static constexpr int DUMMY_OFF = RI_OFF + RI_INSTR * 256;
   static constexpr int STAGE = DUMMY_OFF + (HAS_DUMMY ? 256 : 0);
   static constexpr int PIPE = T::S * STAGE;
 
-  // Stores per wave per finished tile (each a 16-byte buffer store).
+  // Accumulation: threads per workgroup (MFMA waves + epilogue waves) and the two fp32
+  // tile exchange buffers after the ring. A row of R_ROW_CHUNKS 16-byte chunks; chunk c
+  // of row r sits at position c ^ (r % R_ROW_CHUNKS), which keeps both the MFMA-layout
+  // writes and the row-order reads free of bank conflicts.
+  static constexpr int NT = ACC ? 2 * kThreads : kThreads;
+  static constexpr int R_ROW_CHUNKS = T::BN / 4;
+  static constexpr int R_HALF = ACC ? T::BM * T::BN * 4 : 0;
+  static constexpr int R_OFF = PIPE;
+  static constexpr int SCHED_OFF = PIPE + 2 * R_HALF;  // scheduler tables follow
+
+  // Stores per MFMA wave per finished tile (each a 16-byte buffer store); with an
+  // accumulation input the epilogue waves store instead.
   static constexpr int STORES =
-      FP8 ? (VAR == kKGrouped ? T::MJ * T::NI : T::MJ * (T::NI / 2))
-          : (VAR == kKGrouped ? T::MJ2 * T::NI2 * 4 : T::MJ2 * T::NI2 * 2);
+      ACC ? 0
+          : FP8 ? (VAR == kKGrouped ? T::MJ * T::NI : T::MJ * (T::NI / 2))
+                : (VAR == kKGrouped ? T::MJ2 * T::NI2 * 4 : T::MJ2 * T::NI2 * 2);
   static_assert(FP8 || (T::WTM % 32 == 0 && T::WTN % 32 == 0), "BF16 needs 32x32 subtiles");
   static_assert(PER_WAVE * (T::S - 1) + (T::S - 1) * STORES <= 63, "vmcnt range");
-  static_assert(!ACC || (T::BN * 4 <= 1024 && 1024 % (T::BN * 4) == 0 && C_ROW_CHUNKS <= 64),
-                "accumulation tile staging: whole rows per copy");
+  static_assert(!ACC || ((R_ROW_CHUNKS & (R_ROW_CHUNKS - 1)) == 0 && R_ROW_CHUNKS <= 64 &&
+                         (T::BM * T::BN / 4) % 256 == 0),
+                "accumulation exchange: power-of-two row chunks, whole chunks per lane");
   static_assert(!(ACC && VAR != kKGrouped), "accumulation is K-grouped only");
 };
 
-template <class T, int VAR>
+template <class T, int VAR, int NT>
 __device__ __forceinline__ void sched_init(Sched<T, VAR>& S, const Params& p, int* s_tmp,
                                            int* s_flag) {
   const int tid = threadIdx.x;
   S.ntn = (p.N + T::BN - 1) / T::BN;
   if constexpr (VAR == kMasked) {
-    for (int g = tid; g < p.G; g += kThreads) {
+    for (int g = tid; g < p.G; g += NT) {
       int c = p.meta[g];
       c = c < 0 ? 0 : (c > p.rows ? p.rows : c);
       S.s_b[g] = c;
       S.s_a[g] = ((c + T::BM - 1) / T::BM) * S.ntn;
     }
     __syncthreads();
-    S.total = block_exclusive_scan(S.s_a, p.G, s_tmp);
+    S.total = block_exclusive_scan<NT>(S.s_a, p.G, s_tmp);
   } else if constexpr (VAR == kContig) {
     // s_flag (transient, inside the pipeline stages) holds the block flags and then
     // their prefix; valid blocks are packed into s_b in block order.
     const int nb = (p.rows + kContigBlock - 1) / kContigBlock;
-    for (int b = tid; b < nb; b += kThreads) {
+    for (int b = tid; b < nb; b += NT) {
       const int e = p.meta[(long)b * kContigBlock];
       s_flag[b] = (e >= 0 && e < p.G) ? 1 : 0;
     }
     __syncthreads();
-    const int nvalid = block_exclusive_scan(s_flag, nb, s_tmp);
-    for (int b = tid; b < nb; b += kThreads) {
+    const int nvalid = block_exclusive_scan<NT>(s_flag, nb, s_tmp);
+    for (int b = tid; b < nb; b += NT) {
       const int e = p.meta[(long)b * kContigBlock];
       if (e >= 0 && e < p.G) S.s_b[s_flag[b]] = (b << 12) | e;
     }
@@ -134,14 +150,14 @@ __device__ __forceinline__ void sched_init(Sched<T, VAR>& S, const Params& p, in
     S.total = nvalid * (kContigBlock / T::BM) * S.ntn;
   } else {
     S.mtn = (p.rows + T::BM - 1) / T::BM;
-    for (int g = tid; g < p.G; g += kThreads) {
+    for (int g = tid; g < p.G; g += NT) {
       const int k = p.meta[g];
       S.s_b[g] = k;
       S.s_a[g] = k > 0 ? k : 0;
     }
     __syncthreads();
-    block_exclusive_scan(S.s_a, p.G, s_tmp);
-    for (int g = tid; g < p.G; g += kThreads) {
+    block_exclusive_scan<NT>(S.s_a, p.G, s_tmp);
+    for (int g = tid; g < p.G; g += NT) {
       const int k = S.s_b[g];
       const int pe = S.s_a[g];
       const bool usable = k >= 0 && (k % p.k_granule) == 0 && (pe % p.k_granule) == 0 &&
@@ -283,10 +299,94 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
   return t;
 }
 
+// ----------------------------------------------------------------------------- epilogue
+// waves of an accumulating K-grouped call
+
+// Runs on the four epilogue waves (ew = 0..3) from the first tile t0 (logical index L0)
+// onwards. Lane chunk u of a tile is the 16-byte piece q = 256 u + 64 ew + lane in row
+// order (row q / R_ROW_CHUNKS, column chunk q % R_ROW_CHUNKS), so every load and store
+// instruction covers whole 256-byte row segments. The C tile of the k-th tile from now
+// sits in ring slot k % kCPrefetch; the MFMA waves publish tile x in exchange buffer
+// x % 2 with the barrier that follows its last slice.
+template <class T, int VAR, int DT, int GRAN, class Lay>
+__device__ __forceinline__ void accumulate_waves(const Sched<T, VAR>& Sd, const Params& p,
+                                                 const uint8_t* smem, TileCtx t0, long L0,
+                                                 int ew, int lane) {
+  constexpr int ROWC = Lay::R_ROW_CHUNKS;
+  constexpr int PER = T::BM * T::BN / 4 / 256;  // chunks per lane per tile
+  constexpr int P = kCPrefetch;
+  static_assert(P % 2 == 0, "exchange buffer parity follows the ring slot");
+  const int grid = gridDim.x;
+  int rr[PER], cc[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int q = 256 * u + 64 * ew + lane;
+    rr[u] = q / ROWC;
+    cc[u] = q % ROWC;
+  }
+  auto offset = [&](const TileCtx& t, int u) -> uint32_t {
+    const int m = t.m0 + rr[u], n = t.n0 + 4 * cc[u];
+    return (t.valid && m < p.rows && n < p.N) ? (uint32_t)(((long)m * p.N + n) * 4) : kOOB;
+  };
+  v4i ring[P][PER];
+  TileCtx tp = t0;  // prefetch cursor, P tiles ahead of te
+  long Lp = L0;
+  auto prefetch = [&](v4i* slot) {
+    const v4i rs = make_rsrc(tp.d_base, tp.d_bytes);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) slot[u] = load_b128(rs, offset(tp, u));
+    if (tp.valid) {
+      Lp += grid;
+      tp = decode_tile<T, VAR, DT, GRAN>(Sd, p, Lp);
+    }
+  };
+  // Between the first P prefetches go PER dropped stores each (zero-size resource), so
+  // the first pass around the loop sees the same count of younger memory operations as
+  // every later one (a slot's loads are followed by P - 1 tiles' stores and loads).
+#pragma unroll
+  for (int q = 0; q < P; ++q) {
+    prefetch(ring[q]);
+    if (q < P - 1) {
+      const v4i none = make_rsrc(nullptr, 0);
+#pragma unroll
+      for (int u = 0; u < PER; ++u) store_b128(none, kOOB + 16 * u, (v4i){0, 0, 0, 0});
+    }
+  }
+
+  TileCtx te = t0;
+  long Le = L0;
+  int nb = te.nk + 1;  // barriers until the first tile is published
+  while (true) {
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      for (int b = 0; b < nb; ++b) lds_barrier();
+      const uint8_t* R = smem + Lay::R_OFF + (q & 1) * Lay::R_HALF;
+      const v4i rs = make_rsrc(te.d_base, te.d_bytes);
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int pc = cc[u] ^ (rr[u] % ROWC);
+        const v4f r = *reinterpret_cast<const v4f*>(R + rr[u] * T::BN * 4 + pc * 16);
+        const v4i c = ring[q][u];
+        const v4f d = r + (v4f){__int_as_float(c.x), __int_as_float(c.y),
+                                __int_as_float(c.z), __int_as_float(c.w)};
+        store_b128(rs, offset(te, u), (v4i){__float_as_int(d[0]), __float_as_int(d[1]),
+                                           __float_as_int(d[2]), __float_as_int(d[3])});
+      }
+      prefetch(ring[q]);
+      Le += grid;
+      te = decode_tile<T, VAR, DT, GRAN>(Sd, p, Le);
+      nb = te.nk;  // 0 once the sequence has ended: the remaining slots only idle
+    }
+    // The only exit is here, after all P slots, so every path around the loop passes
+    // every slot and the compiler's wait for a slot's C tile stays P - 1 tiles deep.
+    if (!te.valid) return;
+  }
+}
+
 // ----------------------------------------------------------------------------- kernel
 
 template <class T, int VAR, int DT, int SF, int GRAN, bool ACC>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
+__global__ __launch_bounds__(ACC ? 2 * kThreads : kThreads) void grouped_gemm_kernel(Params p) {
   using Lay = Layout<T, VAR, DT, SF, GRAN, ACC>;
   constexpr bool FP8 = Lay::FP8;
   constexpr int NI = T::NI, MJ = T::MJ, S = T::S;
@@ -303,13 +403,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // first copy is issued)
   Sched<T, VAR> Sd;
   {
-    int* base = reinterpret_cast<int*>(smem + Lay::PIPE);
+    int* base = reinterpret_cast<int*>(smem + Lay::SCHED_OFF);
     const int n = (VAR == kContig) ? (p.rows + kContigBlock - 1) / kContigBlock : p.G;
     Sd.s_a = base;
     Sd.s_b = base + (VAR == kContig ? 0 : n);
     int* s_tmp = reinterpret_cast<int*>(smem);
     int* s_flag = s_tmp + kThreads;
-    sched_init<T, VAR>(Sd, p, s_tmp, s_flag);
+    sched_init<T, VAR, Lay::NT>(Sd, p, s_tmp, s_flag);
   }
   const uint32_t lds0 = lds_addr(smem);
   const int grid = gridDim.x;
@@ -326,9 +426,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // valid range); a slice only adds its K offset.
   struct Issue {
     TileCtx t;
-    v4i rs_a, rs_b, rs_d;
+    v4i rs_a, rs_b;
     uint32_t vab[Lay::U_AB];
-    uint32_t vc[Lay::U_C > 0 ? Lay::U_C : 1];
   };
   // Logical 16-byte chunk this lane copies: the LDS row of every copy is 8q + lane / 8
   // (so its low 3 bits are lane / 8) and the chunk is XOR-swizzled with them.
@@ -337,10 +436,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
     const TileCtx& t = I.t;
     I.rs_a = make_rsrc(t.a_base, t.a_bytes);
     I.rs_b = make_rsrc(t.b_base, t.b_bytes);
-    I.rs_d = make_rsrc(t.d_base, t.d_bytes);
     pin_sgpr(I.rs_a);
     pin_sgpr(I.rs_b);
-    pin_sgpr(I.rs_d);
 #pragma unroll
     for (int u = 0; u < Lay::U_AB; ++u) {
       const int R = 8 * (4 * u + wave) + (lane >> 3);
@@ -351,15 +448,6 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
         const int n = t.n0 + weight_row_of_lds<T, !FP8>(R - T::BM);
         I.vab[u] = (t.valid && n < p.N) ? (uint32_t)(n * t.ldb + c16) : kOOB;
       }
-    }
-#pragma unroll
-    for (int u = 0; u < Lay::U_C; ++u) {
-      constexpr int ROWS_PER = 1024 / (T::BN * 4);
-      const int r = (4 * u + wave) * ROWS_PER + lane / Lay::C_ROW_CHUNKS;
-      const int pc = lane % Lay::C_ROW_CHUNKS;
-      const int c = pc ^ (r % Lay::C_ROW_CHUNKS);
-      const int m = t.m0 + r, n = t.n0 + 4 * c;
-      I.vc[u] = (t.valid && m < p.rows && n + 4 <= p.N) ? (uint32_t)(((long)m * p.N + n) * 4) : kOOB;
     }
   };
 
@@ -419,11 +507,6 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
         dma_x1(st + Lay::DUMMY_OFF, rs_meta, kOOB);  // keeps the per-wave count uniform
       }
     }
-    // the accumulation input of a tile is needed by the epilogue of its last slice
-    const bool last = s == t.nk - 1;
-#pragma unroll
-    for (int u = 0; u < Lay::U_C; ++u)
-      dma_x4(st + Lay::C_OFF + 1024 * (4 * u + wave), I.rs_d, last ? I.vc[u] : kOOB);
   };
 
   // ---- per-lane constant LDS offsets of the MFMA fragments (XOR swizzle folded in)
@@ -516,9 +599,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   };
 
   // Row-masked stores of the finished tile: exactly Lay::STORES buffer stores per wave,
-  // lanes outside the valid rows / columns use an out-of-range offset.
-  auto epilogue = [&](const TileCtx& t, int stg) {
+  // lanes outside the valid rows / columns use an out-of-range offset. With an
+  // accumulation input the tile goes to the exchange buffer at byte offset `rx` instead.
+  auto epilogue = [&](const TileCtx& t, int stg, int rx) {
     const uint8_t* st = smem + stg * Lay::STAGE;
+    uint8_t* R = smem + Lay::R_OFF + rx;
     const v4i rs_d = make_rsrc(t.d_base, t.d_bytes);
     if constexpr (FP8) {
       const int nl0 = wn0 + lg * 4 * NI;  // tile-local first column of this lane
@@ -533,11 +618,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
         if constexpr (VAR == kKGrouped) {
 #pragma unroll
           for (int i = 0; i < NI; ++i) {
-            v4f v = acc[i][j];
+            const v4f v = acc[i][j];
             if constexpr (ACC) {
-              const int c = (nl0 + 4 * i) / 4;
-              const int pc = c ^ (rl % Lay::C_ROW_CHUNKS);
-              v += *reinterpret_cast<const v4f*>(st + Lay::C_OFF + rl * T::BN * 4 + pc * 16);
+              const int pc = ((nl0 + 4 * i) / 4) ^ (rl % Lay::R_ROW_CHUNKS);
+              *reinterpret_cast<v4f*>(R + rl * T::BN * 4 + pc * 16) = v;
+              continue;
             }
             const bool ok = row_ok && n_start + 4 * i + 4 <= p.N;
             const uint32_t voff = ok ? (uint32_t)(((long)m * p.N + n_start + 4 * i) * 4) : kOOB;
@@ -575,11 +660,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
           if constexpr (VAR == kKGrouped) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              v4f x = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+              const v4f x = {v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
               if constexpr (ACC) {
-                const int c = nl0 / 4 + q;
-                const int pc = c ^ (rl % Lay::C_ROW_CHUNKS);
-                x += *reinterpret_cast<const v4f*>(st + Lay::C_OFF + rl * T::BN * 4 + pc * 16);
+                const int pc = (nl0 / 4 + q) ^ (rl % Lay::R_ROW_CHUNKS);
+                *reinterpret_cast<v4f*>(R + rl * T::BN * 4 + pc * 16) = x;
+                continue;
               }
               const bool ok = row_ok && n_start + 4 * q + 4 <= p.N;
               const uint32_t voff = ok ? (uint32_t)(((long)m * p.N + n_start + 4 * q) * 4) : kOOB;
@@ -621,6 +706,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
     return false;
   };
   __syncthreads();  // scheduler scratch in stage memory is dead from here on
+  if constexpr (ACC) {
+    if (wave >= 4) {
+      accumulate_waves<T, VAR, DT, GRAN, Lay>(Sd, p, smem, tc, Lc, wave - 4, lane);
+      return;
+    }
+  }
   prepare(ic);
 #pragma unroll
   for (int k = 0; k < S - 1; ++k) {
@@ -631,6 +722,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
   // their stores are younger than the copies waited for below
   unsigned epi_hist = 0;
   int it = 0;
+  int rx = 0;  // exchange buffer of the next finished tile (accumulating calls)
   while (true) {
     vm_wait_steps<Lay::PER_WAVE * (S - 2), Lay::STORES, S - 1>(__builtin_popcount(epi_hist));
     lds_barrier();
@@ -652,12 +744,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(Params p) {
     }
     compute(tc, sc, stg);
     const bool epi = sc == tc.nk - 1;
-    if (epi) epilogue(tc, stg);
+    if (epi) {
+      epilogue(tc, stg, rx);
+      rx ^= Lay::R_HALF;
+    }
     epi_hist = ((epi_hist << 1) | (epi ? 1u : 0u)) & ((1u << (S - 1)) - 1u);
     advance(tc, Lc, sc);
     if (!tc.valid) break;
     ++it;
   }
+  if constexpr (ACC) lds_barrier();  // publishes the last tile to the epilogue waves
 }
 
 }  // namespace mgg
