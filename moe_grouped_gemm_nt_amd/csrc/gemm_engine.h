@@ -253,16 +253,23 @@ extern "C" __device__ void mgg_raw_buffer_store_v4i32(v4i vdata, v4i rsrc, int v
                                                      int soffset, int aux)
     __asm("llvm.amdgcn.raw.buffer.store.v4i32");
 
+// Cache-policy operand of the buffer intrinsics: bit 1 is the gfx950 "nt" (streaming)
+// hint, for data touched once per call.
+constexpr int kCacheDefault = 0;
+constexpr int kCacheStream = 2;
+
+template <int AUX = kCacheDefault>
 __device__ __forceinline__ void store_b128(v4i rsrc, uint32_t voff, v4i v) {
-  mgg_raw_buffer_store_v4i32(v, rsrc, (int)voff, 0, 0);
+  mgg_raw_buffer_store_v4i32(v, rsrc, (int)voff, 0, AUX);
 }
 
 // The matching load into registers; the compiler tracks its completion like any load.
 extern "C" __device__ v4i mgg_raw_buffer_load_v4i32(v4i rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.buffer.load.v4i32");
 
+template <int AUX = kCacheDefault>
 __device__ __forceinline__ v4i load_b128(v4i rsrc, uint32_t voff) {
-  return mgg_raw_buffer_load_v4i32(rsrc, (int)voff, 0, 0);
+  return mgg_raw_buffer_load_v4i32(rsrc, (int)voff, 0, AUX);
 }
 
 }  // namespace mgg

@@ -334,7 +334,7 @@ __device__ __forceinline__ void accumulate_waves(const Sched<T, VAR>& Sd, const 
   auto prefetch = [&](v4i* slot) {
     const v4i rs = make_rsrc(tp.d_base, tp.d_bytes);
 #pragma unroll
-    for (int u = 0; u < PER; ++u) slot[u] = load_b128(rs, offset(tp, u));
+    for (int u = 0; u < PER; ++u) slot[u] = load_b128<kCacheStream>(rs, offset(tp, u));
     if (tp.valid) {
       Lp += grid;
       tp = decode_tile<T, VAR, DT, GRAN>(Sd, p, Lp);
@@ -369,8 +369,9 @@ __device__ __forceinline__ void accumulate_waves(const Sched<T, VAR>& Sd, const 
         const v4i c = ring[q][u];
         const v4f d = r + (v4f){__int_as_float(c.x), __int_as_float(c.y),
                                 __int_as_float(c.z), __int_as_float(c.w)};
-        store_b128(rs, offset(te, u), (v4i){__float_as_int(d[0]), __float_as_int(d[1]),
-                                           __float_as_int(d[2]), __float_as_int(d[3])});
+        store_b128<kCacheStream>(rs, offset(te, u),
+                                 (v4i){__float_as_int(d[0]), __float_as_int(d[1]),
+                                       __float_as_int(d[2]), __float_as_int(d[3])});
       }
       prefetch(ring[q]);
       Le += grid;
@@ -546,13 +547,13 @@ __global__ __launch_bounds__(ACC ? 2 * kThreads : kThreads) void grouped_gemm_ke
           sbw = ue8m0_to_float(st[Lay::SB_OFF + 4 * lb + (int)(ob & 3)]);
         }
       }
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
+      // Weight fragment i (and its per-channel scales) from LDS.
+      auto load_w = [&](int i, v8i& afr, v4f& sbv) {
         const uint8_t* rp = st + Lay::B_OFF + (wn0 + 16 * i + lr) * kSliceBytes;
         const v4i lo = *reinterpret_cast<const v4i*>(rp + x_lo);
         const v4i hi = *reinterpret_cast<const v4i*>(rp + x_hi);
-        const v8i afr = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        v4f sbv = {sbw, sbw, sbw, sbw};
+        afr = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        sbv = (v4f){sbw, sbw, sbw, sbw};
         if constexpr (GRAN == kSfbChannel) {
           const int col = wn0 + lg * 4 * NI + 4 * i;
           if constexpr (SF == kSfF32) {
@@ -564,16 +565,37 @@ __global__ __launch_bounds__(ACC ? 2 * kThreads : kThreads) void grouped_gemm_ke
                         ue8m0_to_float(bp[3])};
           }
         }
+      };
+      // Software pipeline over the weight fragments: the MJ partial sums of fragment
+      // i + 1 are issued before fragment i is promoted, so consecutive MFMAs are
+      // independent and the promotion FMAs overlap them (format 0 = FP8 E4M3 for both
+      // operands; scale exponent 127 = 2^0).
+      const v4f zero = {0.f, 0.f, 0.f, 0.f};
+      v4f part[2][MJ];
+      v8i afr;
+      v4f sbv;
+      load_w(0, afr, sbv);
 #pragma unroll
-        for (int j = 0; j < MJ; ++j) {
-          const v4f zero = {0.f, 0.f, 0.f, 0.f};
-          // format 0 = FP8 E4M3 for both operands; scale exponent 127 = 2^0
-          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], zero,
-                                                                           0, 0, 0, 127, 0, 127);
+      for (int j = 0; j < MJ; ++j)
+        part[0][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], zero, 0, 0, 0,
+                                                                      127, 0, 127);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        v4f sbv_next = sbv;
+        if (i + 1 < NI) {
+          v8i afr_next;
+          load_w(i + 1, afr_next, sbv_next);
+#pragma unroll
+          for (int j = 0; j < MJ; ++j)
+            part[(i + 1) & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                afr_next, bfr[j], zero, 0, 0, 0, 127, 0, 127);
+        }
+#pragma unroll
+        for (int j = 0; j < MJ; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            acc[i][j][r] = __builtin_fmaf(part[r], sa[j] * sbv[r], acc[i][j][r]);
-        }
+            acc[i][j][r] = __builtin_fmaf(part[i & 1][j][r], sa[j] * sbv[r], acc[i][j][r]);
+        sbv = sbv_next;
       }
     } else {
       // 32x32x16 MFMAs: MFMA h of the slice takes K elements 16h .. 16h + 15; lane group
