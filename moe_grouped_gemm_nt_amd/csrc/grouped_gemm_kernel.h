@@ -566,36 +566,36 @@ __global__ __launch_bounds__(ACC ? 2 * kThreads : kThreads) void grouped_gemm_ke
           }
         }
       };
-      // Software pipeline over the weight fragments: the MJ partial sums of fragment
-      // i + 1 are issued before fragment i is promoted, so consecutive MFMAs are
-      // independent and the promotion FMAs overlap them (format 0 = FP8 E4M3 for both
+      // Software pipeline over the weight fragments: fragment i + 2 is read from LDS
+      // while the MJ partial sums of fragment i + 1 are issued and fragment i is
+      // promoted, so consecutive MFMAs are independent, the promotion FMAs overlap
+      // them and LDS latency stays off the critical path (format 0 = FP8 E4M3 for both
       // operands; scale exponent 127 = 2^0).
       const v4f zero = {0.f, 0.f, 0.f, 0.f};
       v4f part[2][MJ];
-      v8i afr;
-      v4f sbv;
-      load_w(0, afr, sbv);
+      v8i wf[3];
+      v4f sv[3];
+      load_w(0, wf[0], sv[0]);
+      if (NI > 1) load_w(1, wf[1], sv[1]);
 #pragma unroll
       for (int j = 0; j < MJ; ++j)
-        part[0][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], zero, 0, 0, 0,
-                                                                      127, 0, 127);
+        part[0][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[0], bfr[j], zero, 0, 0,
+                                                                      0, 127, 0, 127);
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        v4f sbv_next = sbv;
+        if (i + 2 < NI) load_w(i + 2, wf[(i + 2) % 3], sv[(i + 2) % 3]);
         if (i + 1 < NI) {
-          v8i afr_next;
-          load_w(i + 1, afr_next, sbv_next);
 #pragma unroll
           for (int j = 0; j < MJ; ++j)
             part[(i + 1) & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                afr_next, bfr[j], zero, 0, 0, 0, 127, 0, 127);
+                wf[(i + 1) % 3], bfr[j], zero, 0, 0, 0, 127, 0, 127);
         }
 #pragma unroll
         for (int j = 0; j < MJ; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            acc[i][j][r] = __builtin_fmaf(part[i & 1][j][r], sa[j] * sbv[r], acc[i][j][r]);
-        sbv = sbv_next;
+            acc[i][j][r] =
+                __builtin_fmaf(part[i & 1][j][r], sa[j] * sv[i % 3][r], acc[i][j][r]);
       }
     } else {
       // 32x32x16 MFMAs: MFMA h of the slice takes K elements 16h .. 16h + 15; lane group
