@@ -601,21 +601,28 @@ __global__ __launch_bounds__(ACC ? 2 * kThreads : kThreads) void grouped_gemm_ke
       // 32x32x16 MFMAs: MFMA h of the slice takes K elements 16h .. 16h + 15; lane group
       // g = lane / 32 supplies elements 16h + 8g .. 16h + 8g + 7, the 16-byte chunk
       // 2h + g of its row.
+      // The fragments of step h + 1 are read from LDS while the MFMAs of step h run.
       const int l32 = lane & 31, g2 = lane >> 5;
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
+      v8bf bf[2][MJ2], wf[2][NI2];
+      auto load_h = [&](int h, v8bf* b, v8bf* w) {
         const int xo = ((2 * h + g2) ^ (l32 & 7)) << 4;
-        v8bf bfr[MJ2];
 #pragma unroll
         for (int j = 0; j < MJ2; ++j)
-          bfr[j] = *reinterpret_cast<const v8bf*>(st + Lay::A_OFF + (wm0 + 32 * j + l32) * kSliceBytes + xo);
+          b[j] = *reinterpret_cast<const v8bf*>(st + Lay::A_OFF + (wm0 + 32 * j + l32) * kSliceBytes + xo);
 #pragma unroll
-        for (int i = 0; i < NI2; ++i) {
-          const v8bf afr = *reinterpret_cast<const v8bf*>(st + Lay::B_OFF + (wn0 + 32 * i + l32) * kSliceBytes + xo);
+        for (int i = 0; i < NI2; ++i)
+          w[i] = *reinterpret_cast<const v8bf*>(st + Lay::B_OFF + (wn0 + 32 * i + l32) * kSliceBytes + xo);
+      };
+      load_h(0, bf[0], wf[0]);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        if (h + 1 < 4) load_h(h + 1, bf[(h + 1) & 1], wf[(h + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < NI2; ++i)
 #pragma unroll
           for (int j = 0; j < MJ2; ++j)
-            acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afr, bfr[j], acc2[i][j], 0, 0, 0);
-        }
+            acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[h & 1][i], bf[h & 1][j],
+                                                                 acc2[i][j], 0, 0, 0);
       }
     }
   };
