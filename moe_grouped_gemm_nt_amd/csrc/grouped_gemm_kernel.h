@@ -98,7 +98,7 @@ struct Layout {
   // tile exchange buffers after the ring. A row of R_ROW_CHUNKS 16-byte chunks; chunk c
   // of row r sits at position c ^ (r % R_ROW_CHUNKS), which keeps both the MFMA-layout
   // writes and the row-order reads free of bank conflicts.
-  static constexpr int NT = ACC ? 2 * kThreads : kThreads;
+  static constexpr int NT = 2 * kThreads;
   static constexpr int R_ROW_CHUNKS = T::BN / 4;
   static constexpr int R_HALF = ACC ? T::BM * T::BN * 4 : 0;
   static constexpr int R_OFF = PIPE;
@@ -387,7 +387,7 @@ __device__ __forceinline__ void accumulate_waves(const Sched<T, VAR>& Sd, const 
 // ----------------------------------------------------------------------------- kernel
 
 template <class T, int VAR, int DT, int SF, int GRAN, bool ACC>
-__global__ __launch_bounds__(ACC ? 2 * kThreads : kThreads) void grouped_gemm_kernel(Params p) {
+__global__ __launch_bounds__(2 * kThreads) void grouped_gemm_kernel(Params p) {
   using Lay = Layout<T, VAR, DT, SF, GRAN, ACC>;
   constexpr bool FP8 = Lay::FP8;
   constexpr int NI = T::NI, MJ = T::MJ, S = T::S;
@@ -396,6 +396,7 @@ __global__ __launch_bounds__(ACC ? 2 * kThreads : kThreads) void grouped_gemm_ke
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cwave = wave & 3;  // slot index of a wave that issues operand copies
   const int lr = lane & 15, lg = lane >> 4;
   const int wave_m = wave / T::WN, wave_n = wave % T::WN;
   const int wm0 = wave_m * T::WTM, wn0 = wave_n * T::WTN;
@@ -441,7 +442,7 @@ __global__ __launch_bounds__(ACC ? 2 * kThreads : kThreads) void grouped_gemm_ke
     pin_sgpr(I.rs_b);
 #pragma unroll
     for (int u = 0; u < Lay::U_AB; ++u) {
-      const int R = 8 * (4 * u + wave) + (lane >> 3);
+      const int R = 8 * (4 * u + cwave) + (lane >> 3);
       if (u < Lay::U_A) {
         const int m = t.m0 + R;
         I.vab[u] = (t.valid && m < t.a_lim) ? (uint32_t)(m * t.lda + c16) : kOOB;
@@ -465,11 +466,11 @@ __global__ __launch_bounds__(ACC ? 2 * kThreads : kThreads) void grouped_gemm_ke
     for (int u = 0; u < Lay::U_AB; ++u) {
       uint32_t voff = I.vab[u] + kb0;
       if (!full && kb0 + c16 + 16 > t.k_bytes) voff = kOOB;
-      dma_x4(st + Lay::A_OFF + 1024 * (4 * u + wave), u < Lay::U_A ? I.rs_a : I.rs_b, voff);
+      dma_x4(st + Lay::A_OFF + 1024 * (4 * u + cwave), u < Lay::U_A ? I.rs_a : I.rs_b, voff);
     }
 #pragma unroll
     for (int us = 0; us < Lay::U_SM; ++us) {
-      const int e = 4 * us + wave;  // small-copy index dealt to this wave (uniform)
+      const int e = 4 * us + cwave;  // small-copy index dealt to this wave (uniform)
       if (e < Lay::SA_INSTR) {
         const int l = 64 * e + lane;
         const long o = t.sfa_off + (long)s * t.sfa_ld + t.m0;
@@ -741,23 +742,49 @@ __global__ __launch_bounds__(ACC ? 2 * kThreads : kThreads) void grouped_gemm_ke
       return;
     }
   }
+  // The operand copies are issued by waves 4..7 when they are free (the MFMA waves
+  // then never wait to enter the memory pipeline), else by the MFMA waves themselves.
+  if (!ACC && wave < 4) goto mfma_loop;
   prepare(ic);
 #pragma unroll
   for (int k = 0; k < S - 1; ++k) {
     issue(ic, si, k);
     if (advance(ic.t, Li, si)) prepare(ic);
   }
+  if constexpr (!ACC) {
+    // Copy waves: one barrier per item, like the MFMA waves. Before barrier j the
+    // copies of item j have landed (the PER_WAVE * (S - 2) younger ones may still be in
+    // flight); after it the stage of item j + S - 1 is free and is refilled.
+    TileCtx tm = tc;  // mirror of the compute cursor: the same number of barriers
+    long Lm = Lc;
+    int sm = 0, jt = 0;
+    while (true) {
+      vm_wait_imm<Lay::PER_WAVE * (S - 2)>();
+      lds_barrier();
+      issue(ic, si, (jt + S - 1) % S);
+      if (advance(ic.t, Li, si)) prepare(ic);
+      advance(tm, Lm, sm);
+      if (!tm.valid) break;
+      ++jt;
+    }
+    vm_wait_imm<0>();  // the last (idle) copies land before the workgroup's LDS is released
+    return;
+  }
+mfma_loop:
   // whether each of the last S-1 iterations ran an epilogue (uniform), newest in bit 0;
   // their stores are younger than the copies waited for below
   unsigned epi_hist = 0;
   int it = 0;
   int rx = 0;  // exchange buffer of the next finished tile (accumulating calls)
   while (true) {
-    vm_wait_steps<Lay::PER_WAVE * (S - 2), Lay::STORES, S - 1>(__builtin_popcount(epi_hist));
+    if constexpr (ACC)
+      vm_wait_steps<Lay::PER_WAVE * (S - 2), Lay::STORES, S - 1>(__builtin_popcount(epi_hist));
     lds_barrier();
     const int stg = it % S;
-    issue(ic, si, (it + S - 1) % S);
-    if (advance(ic.t, Li, si)) prepare(ic);
+    if constexpr (ACC) {
+      issue(ic, si, (it + S - 1) % S);
+      if (advance(ic.t, Li, si)) prepare(ic);
+    }
     if (sc == 0) {
       if constexpr (FP8) {
 #pragma unroll
