@@ -231,20 +231,10 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// s_waitcnt vmcnt(BASE + k * STEP) for a run-time k in [0, KMAX] (uniform); vmcnt
-// holds at most 63, and a smaller count than needed only waits longer.
+// s_waitcnt vmcnt(N): at most N of this wave's vector-memory operations outstanding.
 template <int N>
 __device__ __forceinline__ void vm_wait_imm() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N < 63 ? N : 63) : "memory");
-}
-template <int BASE, int STEP, int K>
-__device__ __forceinline__ void vm_wait_steps(int k) {
-  if constexpr (K == 0) {
-    vm_wait_imm<BASE>();
-  } else {
-    if (k >= K) vm_wait_imm<BASE + K * STEP>();
-    else vm_wait_steps<BASE, STEP, K - 1>(k);
-  }
 }
 
 // The LLVM raw buffer store intrinsic, declared with the 128-bit resource as a plain

@@ -3,24 +3,25 @@
 // instantiates it for every (tile, variant, dtype, scale format, weight-scale
 // granularity, accumulation) combination the host dispatcher can pick.
 //
-// Pipeline. A workgroup walks a flat sequence of work items (tile, 128-byte K slice).
-// Two cursors run over the same sequence: the issue cursor starts the direct
-// global -> LDS copies of item i + S - 1 into ring stage (i + S - 1) % S while the
-// compute cursor runs the MFMAs of item i from stage i % S. Each wave issues the same
-// number of copy instructions for every item (out-of-range lanes and idle items copy
-// zeros), and every store of the epilogue is issued unconditionally (masked lanes use
-// an out-of-range offset), so each wave knows exactly how many of its vector-memory
-// operations are younger than the copies of item i and waits for exactly those
-// (vmcnt counts in issue order). One barrier per item then makes every wave's copies
-// visible and guarantees the stage about to be refilled is no longer being read.
-//
-// Accumulating K-grouped calls (D = C + A B^T) add four epilogue waves. The MFMA waves
-// write each finished tile into one of two LDS exchange buffers instead of storing it;
-// the epilogue waves keep the C tiles of the next kCPrefetch tiles in flight in their
-// registers, and after the barrier that publishes a tile they add it to its C tile
-// and store D. Both wave groups walk the same tile sequence and execute the same
-// number of barriers (the MFMA waves one per item plus a final one, the epilogue waves
-// the same count arranged per tile), so the exchange needs no other synchronisation.
+// Pipeline. A workgroup walks a flat sequence of work items (tile, 128-byte K slice)
+// with three groups of four waves (two without an accumulation input):
+//   - copy waves run the issue cursor: they start the direct global -> LDS copies of
+//     item i + S - 1 into ring stage (i + S - 1) % S. Each copy wave issues the same
+//     number of copy instructions for every item (out-of-range lanes and idle items
+//     copy zeros), so before the barrier of item i it waits (vmcnt counts in issue
+//     order) for exactly its copies of item i;
+//   - MFMA waves run the compute cursor: the MFMAs of item i from stage i % S and, on a
+//     tile's last slice, the epilogue. They never issue copies, so they never stall
+//     waiting to enter the memory pipeline;
+//   - with an accumulation input (K-grouped D = C + A B^T), epilogue waves: the MFMA
+//     waves write each finished tile into one of two LDS exchange buffers instead of
+//     storing it; the epilogue waves keep the C tiles of the next kCPrefetch tiles in
+//     flight in their registers, and after the barrier that publishes a tile they add
+//     it to its C tile and store D.
+// One barrier per item makes the copies of item i visible and guarantees that the stage
+// about to be refilled is no longer being read. Every group walks the same tile
+// sequence and executes the same number of barriers (one per item, plus a final one
+// that publishes the last exchange tile), so nothing else needs synchronising.
 #pragma once
 
 #include "gemm_engine.h"
@@ -98,20 +99,14 @@ struct Layout {
   // tile exchange buffers after the ring. A row of R_ROW_CHUNKS 16-byte chunks; chunk c
   // of row r sits at position c ^ (r % R_ROW_CHUNKS), which keeps both the MFMA-layout
   // writes and the row-order reads free of bank conflicts.
-  static constexpr int NT = 2 * kThreads;
+  static constexpr int NT = (ACC ? 3 : 2) * kThreads;
   static constexpr int R_ROW_CHUNKS = T::BN / 4;
   static constexpr int R_HALF = ACC ? T::BM * T::BN * 4 : 0;
   static constexpr int R_OFF = PIPE;
   static constexpr int SCHED_OFF = PIPE + 2 * R_HALF;  // scheduler tables follow
 
-  // Stores per MFMA wave per finished tile (each a 16-byte buffer store); with an
-  // accumulation input the epilogue waves store instead.
-  static constexpr int STORES =
-      ACC ? 0
-          : FP8 ? (VAR == kKGrouped ? T::MJ * T::NI : T::MJ * (T::NI / 2))
-                : (VAR == kKGrouped ? T::MJ2 * T::NI2 * 4 : T::MJ2 * T::NI2 * 2);
   static_assert(FP8 || (T::WTM % 32 == 0 && T::WTN % 32 == 0), "BF16 needs 32x32 subtiles");
-  static_assert(PER_WAVE * (T::S - 1) + (T::S - 1) * STORES <= 63, "vmcnt range");
+  static_assert(PER_WAVE * (T::S - 1) <= 63, "vmcnt range of a copy wave");
   static_assert(!ACC || ((R_ROW_CHUNKS & (R_ROW_CHUNKS - 1)) == 0 && R_ROW_CHUNKS <= 64 &&
                          (T::BM * T::BN / 4) % 256 == 0),
                 "accumulation exchange: power-of-two row chunks, whole chunks per lane");
@@ -387,7 +382,7 @@ __device__ __forceinline__ void accumulate_waves(const Sched<T, VAR>& Sd, const 
 // ----------------------------------------------------------------------------- kernel
 
 template <class T, int VAR, int DT, int SF, int GRAN, bool ACC>
-__global__ __launch_bounds__(2 * kThreads) void grouped_gemm_kernel(Params p) {
+__global__ __launch_bounds__((ACC ? 3 : 2) * kThreads) void grouped_gemm_kernel(Params p) {
   using Lay = Layout<T, VAR, DT, SF, GRAN, ACC>;
   constexpr bool FP8 = Lay::FP8;
   constexpr int NI = T::NI, MJ = T::MJ, S = T::S;
@@ -628,8 +623,8 @@ __global__ __launch_bounds__(2 * kThreads) void grouped_gemm_kernel(Params p) {
     }
   };
 
-  // Row-masked stores of the finished tile: exactly Lay::STORES buffer stores per wave,
-  // lanes outside the valid rows / columns use an out-of-range offset. With an
+  // Row-masked stores of the finished tile: lanes outside the valid rows / columns use
+  // an out-of-range offset. With an
   // accumulation input the tile goes to the exchange buffer at byte offset `rx` instead.
   auto epilogue = [&](const TileCtx& t, int stg, int rx) {
     const uint8_t* st = smem + stg * Lay::STAGE;
@@ -737,24 +732,22 @@ __global__ __launch_bounds__(2 * kThreads) void grouped_gemm_kernel(Params p) {
   };
   __syncthreads();  // scheduler scratch in stage memory is dead from here on
   if constexpr (ACC) {
-    if (wave >= 4) {
+    if (wave >= 4 && wave < 8) {
       accumulate_waves<T, VAR, DT, GRAN, Lay>(Sd, p, smem, tc, Lc, wave - 4, lane);
       return;
     }
   }
-  // The operand copies are issued by waves 4..7 when they are free (the MFMA waves
-  // then never wait to enter the memory pipeline), else by the MFMA waves themselves.
-  if (!ACC && wave < 4) goto mfma_loop;
-  prepare(ic);
+  if (wave >= (ACC ? 8 : 4)) {
+    // Copy waves (the last four): one barrier per item, like the MFMA waves. Before
+    // barrier j the copies of item j have landed (the PER_WAVE * (S - 2) younger ones
+    // may still be in flight); after it the stage of item j + S - 1 is free and is
+    // refilled. The MFMA waves therefore never wait to enter the memory pipeline.
+    prepare(ic);
 #pragma unroll
-  for (int k = 0; k < S - 1; ++k) {
-    issue(ic, si, k);
-    if (advance(ic.t, Li, si)) prepare(ic);
-  }
-  if constexpr (!ACC) {
-    // Copy waves: one barrier per item, like the MFMA waves. Before barrier j the
-    // copies of item j have landed (the PER_WAVE * (S - 2) younger ones may still be in
-    // flight); after it the stage of item j + S - 1 is free and is refilled.
+    for (int k = 0; k < S - 1; ++k) {
+      issue(ic, si, k);
+      if (advance(ic.t, Li, si)) prepare(ic);
+    }
     TileCtx tm = tc;  // mirror of the compute cursor: the same number of barriers
     long Lm = Lc;
     int sm = 0, jt = 0;
@@ -767,24 +760,16 @@ __global__ __launch_bounds__(2 * kThreads) void grouped_gemm_kernel(Params p) {
       if (!tm.valid) break;
       ++jt;
     }
+    if constexpr (ACC) lds_barrier();  // the MFMA waves' final exchange barrier
     vm_wait_imm<0>();  // the last (idle) copies land before the workgroup's LDS is released
     return;
   }
-mfma_loop:
-  // whether each of the last S-1 iterations ran an epilogue (uniform), newest in bit 0;
-  // their stores are younger than the copies waited for below
-  unsigned epi_hist = 0;
+  // MFMA waves
   int it = 0;
   int rx = 0;  // exchange buffer of the next finished tile (accumulating calls)
   while (true) {
-    if constexpr (ACC)
-      vm_wait_steps<Lay::PER_WAVE * (S - 2), Lay::STORES, S - 1>(__builtin_popcount(epi_hist));
     lds_barrier();
     const int stg = it % S;
-    if constexpr (ACC) {
-      issue(ic, si, (it + S - 1) % S);
-      if (advance(ic.t, Li, si)) prepare(ic);
-    }
     if (sc == 0) {
       if constexpr (FP8) {
 #pragma unroll
@@ -804,7 +789,6 @@ mfma_loop:
       epilogue(tc, stg, rx);
       rx ^= Lay::R_HALF;
     }
-    epi_hist = ((epi_hist << 1) | (epi ? 1u : 0u)) & ((1u << (S - 1)) - 1u);
     advance(tc, Lc, sc);
     if (!tc.valid) break;
     ++it;
