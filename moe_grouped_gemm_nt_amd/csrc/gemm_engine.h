@@ -48,7 +48,7 @@ enum DType { kBF16 = 0, kFP8 = 1 };
 enum SfFmt { kSfF32 = 0, kSfUE8M0 = 1 };
 enum SfbGran { kSfbBlock = 0, kSfbChannel = 1 };
 
-constexpr int kThreads = 256;     // the MFMA waves of a workgroup
+constexpr int kThreads = 256;     // one group of four waves
 // Tiles of accumulation input in flight per epilogue wave. Deeper prefetch measured
 // slower on the K-grouped wgrad shape: the extra C loads queue in front of the MFMA
 // waves' operand copies in the CU's memory pipeline.
@@ -77,12 +77,14 @@ struct Params {
   uint32_t meta_bytes;            // bytes of the routing tensor
 };
 
-// Tile configuration: BM activation rows x BN weight rows per workgroup; 4 waves laid
-// out WM (along m) x WN (along n); S pipeline stages of 128-byte K slices in LDS.
+// Tile configuration: BM activation rows x BN weight rows per workgroup; WM x WN MFMA
+// waves (four or eight) laid out WM along m and WN along n; S pipeline stages of
+// 128-byte K slices in LDS.
 template <int BM_, int BN_, int WM_, int WN_, int S_>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_;
-  static_assert(WM * WN == 4, "four waves per workgroup");
+  static constexpr int NMW = WM * WN;  // MFMA waves
+  static_assert(NMW == 4 || NMW == 8, "four or eight MFMA waves");
   static_assert(S >= 2 && S <= 6, "pipeline depth");
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   // FP8 runs 16x16x128 MFMAs (MJ x NI subtiles per wave); BF16 runs 32x32x16 MFMAs

@@ -99,7 +99,10 @@ struct Layout {
   // tile exchange buffers after the ring. A row of R_ROW_CHUNKS 16-byte chunks; chunk c
   // of row r sits at position c ^ (r % R_ROW_CHUNKS), which keeps both the MFMA-layout
   // writes and the row-order reads free of bank conflicts.
-  static constexpr int NT = (ACC ? 3 : 2) * kThreads;
+  static constexpr int EPI0 = T::NMW;                   // first epilogue wave
+  static constexpr int COPY0 = T::NMW + (ACC ? 4 : 0);  // first of the four copy waves
+  static constexpr int NT = (COPY0 + 4) * 64;
+  static_assert(!ACC || T::NMW == 4, "accumulating tiles use four MFMA waves");
   static constexpr int R_ROW_CHUNKS = T::BN / 4;
   static constexpr int R_HALF = ACC ? T::BM * T::BN * 4 : 0;
   static constexpr int R_OFF = PIPE;
@@ -382,7 +385,8 @@ __device__ __forceinline__ void accumulate_waves(const Sched<T, VAR>& Sd, const 
 // ----------------------------------------------------------------------------- kernel
 
 template <class T, int VAR, int DT, int SF, int GRAN, bool ACC>
-__global__ __launch_bounds__((ACC ? 3 : 2) * kThreads) void grouped_gemm_kernel(Params p) {
+__global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void grouped_gemm_kernel(
+    Params p) {
   using Lay = Layout<T, VAR, DT, SF, GRAN, ACC>;
   constexpr bool FP8 = Lay::FP8;
   constexpr int NI = T::NI, MJ = T::MJ, S = T::S;
@@ -391,7 +395,7 @@ __global__ __launch_bounds__((ACC ? 3 : 2) * kThreads) void grouped_gemm_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int cwave = wave & 3;  // slot index of a wave that issues operand copies
+  const int cwave = (wave - Lay::COPY0) & 3;  // slot index of a copy wave
   const int lr = lane & 15, lg = lane >> 4;
   const int wave_m = wave / T::WN, wave_n = wave % T::WN;
   const int wm0 = wave_m * T::WTM, wn0 = wave_n * T::WTN;
@@ -517,7 +521,56 @@ __global__ __launch_bounds__((ACC ? 3 : 2) * kThreads) void grouped_gemm_kernel(
   // MFMA work of one slice held in stage `stg`.
   auto compute = [&](const TileCtx& t, int s, int stg) {
     const uint8_t* st = smem + stg * Lay::STAGE;
-    if constexpr (FP8) {
+    if constexpr (FP8 && SF == kSfUE8M0) {
+      // Power-of-two scales: the MFMA applies them itself (its E8M0 operand scales, one
+      // per lane for the K elements that lane supplies, here all 128 of the slice) and
+      // accumulates into the tile accumulator, so no promotion instructions are needed:
+      // the weight scale goes with the first operand (weight rows), the activation
+      // scale with the second (activation rows).
+      v8i bfr[MJ];
+      int sab[MJ];
+      const long oa = t.sfa_off + (long)s * t.sfa_ld + t.m0;
+#pragma unroll
+      for (int j = 0; j < MJ; ++j) {
+        const int row = wm0 + 16 * j + lr;
+        const uint8_t* rp = st + Lay::A_OFF + row * kSliceBytes;
+        const v4i lo = *reinterpret_cast<const v4i*>(rp + x_lo);
+        const v4i hi = *reinterpret_cast<const v4i*>(rp + x_hi);
+        bfr[j] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        sab[j] = st[Lay::SA_OFF + (int)(oa & 3) + row];
+      }
+      int sbw = 0;
+      if constexpr (GRAN == kSfbBlock) {
+        const int lb = ((t.n0 & 127) + wn0) >> 7;
+        const long ob = t.sfb_off + (long)(t.n0 / 128 + lb) * t.sfb_ld + s;
+        sbw = st[Lay::SB_OFF + 4 * lb + (int)(ob & 3)];
+      }
+      // Weight fragment i and the scale of the weight row this lane supplies.
+      auto load_w = [&](int i, v8i& afr, int& sb) {
+        const int R = wn0 + 16 * i + lr;
+        const uint8_t* rp = st + Lay::B_OFF + R * kSliceBytes;
+        const v4i lo = *reinterpret_cast<const v4i*>(rp + x_lo);
+        const v4i hi = *reinterpret_cast<const v4i*>(rp + x_hi);
+        afr = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        sb = sbw;
+        if constexpr (GRAN == kSfbChannel) {
+          const long ob = t.sfb_off + (long)s * t.sfb_ld + t.n0;
+          sb = st[Lay::SB_OFF + (int)(ob & 3) + weight_row_of_lds<T, false>(R)];
+        }
+      };
+      v8i wf[3];
+      int sw[3];
+      load_w(0, wf[0], sw[0]);
+      if (NI > 1) load_w(1, wf[1], sw[1]);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        if (i + 2 < NI) load_w(i + 2, wf[(i + 2) % 3], sw[(i + 2) % 3]);
+#pragma unroll
+        for (int j = 0; j < MJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              wf[i % 3], bfr[j], acc[i][j], 0, 0, 0, sw[i % 3], 0, sab[j]);
+      }
+    } else if constexpr (FP8) {
       v8i bfr[MJ];
       float sa[MJ];
       const long oa = t.sfa_off + (long)s * t.sfa_ld + t.m0;
@@ -732,12 +785,12 @@ __global__ __launch_bounds__((ACC ? 3 : 2) * kThreads) void grouped_gemm_kernel(
   };
   __syncthreads();  // scheduler scratch in stage memory is dead from here on
   if constexpr (ACC) {
-    if (wave >= 4 && wave < 8) {
-      accumulate_waves<T, VAR, DT, GRAN, Lay>(Sd, p, smem, tc, Lc, wave - 4, lane);
+    if (wave >= Lay::EPI0 && wave < Lay::COPY0) {
+      accumulate_waves<T, VAR, DT, GRAN, Lay>(Sd, p, smem, tc, Lc, wave - Lay::EPI0, lane);
       return;
     }
   }
-  if (wave >= (ACC ? 8 : 4)) {
+  if (wave >= Lay::COPY0) {
     // Copy waves (the last four): one barrier per item, like the MFMA waves. Before
     // barrier j the copies of item j have landed (the PER_WAVE * (S - 2) younger ones
     // may still be in flight); after it the stage of item j + S - 1 is free and is
