@@ -18,6 +18,8 @@
  *                            token slice, with per-channel scales on both operands
  *                            (DeepGEMM issue "Non-deterministic numerical problem of
  *                            k_grouped_fp8_gemm_nt_contiguous", section "repro script").
+ * The contiguous and K-grouped products also take their routing as per-expert prefix
+ * sums (the "_psum" entry points).
  *
  * Common rules for every entry point:
  *  - Every pointer is caller-owned device memory; the caller allocates every output.
@@ -113,6 +115,35 @@ mgg_status grouped_gemm_contiguous(mgg_dtype dt, int G, int M, int N, int K,
                                    hipStream_t stream);
 
 /*
+ * M-grouped NT GEMM, contiguous rows in prefix-sum ("psum") layout: the routing is one
+ * cumulative row end per expert instead of one expert index per row. The pages name this
+ * mode (DeepGEMM issue "Non-deterministic numerical problem of
+ * k_grouped_fp8_gemm_nt_contiguous", repro script: the use_psum_layout argument; DeepGEMM
+ * issue "SM120 m_grouped_fp8 contiguous kernel: illegal memory access at CUDA graph
+ * replay", verification comment: the psum mode of its graph-mutation test) without
+ * describing it; the reading implemented here: expert e owns rows [start_e, end_e) with
+ *   end_e   = clamp(psum[e], 0, M) raised to the largest end_j of any j < e,
+ *   start_e = end_{e-1} (0 for e = 0),
+ * so segments are consecutive, never overlap and need no alignment.
+ * D[r, :] = A[r, :] . B[e]^T for r in [start_e, end_e); rows at or beyond end_{G-1} are
+ * not written.
+ *
+ *   A           [M][K] (bf16 or e4m3 bytes), 16-byte aligned.
+ *   SFA         FP8 only: [K/128][M].
+ *   B, SFB      as for grouped_gemm_masked.
+ *   D           bf16 [M][N], 16-byte aligned.
+ *   psum        device int32 [G], read by the kernel on every launch (graph-replay safe).
+ *   expected_m  rows per expert hint (<= 0: unknown); never changes results.
+ * Errors: as grouped_gemm_masked.
+ */
+mgg_status grouped_gemm_contiguous_psum(mgg_dtype dt, int G, int M, int N, int K,
+                                        const void* A, const void* SFA,
+                                        const void* B, const void* SFB,
+                                        mgg_sf_fmt sf, mgg_sfb_gran gran,
+                                        void* D, const int32_t* psum, int expected_m,
+                                        hipStream_t stream);
+
+/*
  * K-grouped NT GEMM (weight gradient): expert e owns k_e = ks[e] consecutive tokens
  * starting at token p_e = sum_{j<e} max(ks[j], 0). Operand blocks are packed per
  * expert, tokens contiguous:
@@ -137,6 +168,22 @@ mgg_status grouped_gemm_kgrouped(mgg_dtype dt, int G, int M, int N, int K_total,
                                  mgg_sf_fmt sf,
                                  float* D, const int32_t* ks, int accumulate,
                                  hipStream_t stream);
+
+/*
+ * K-grouped NT GEMM with the token counts in prefix-sum ("psum") layout (the
+ * use_psum_layout argument of the K-grouped call in the repro script of the DeepGEMM issue
+ * "Non-deterministic numerical problem of k_grouped_fp8_gemm_nt_contiguous", not
+ * described there): psum[e] is the
+ * cumulative token end of expert e, so k_e = psum[e] - psum[e-1] (psum[-1] = 0); then
+ * exactly as grouped_gemm_kgrouped with ks[e] = k_e (a decreasing entry gives a negative
+ * k_e: that expert is skipped).
+ */
+mgg_status grouped_gemm_kgrouped_psum(mgg_dtype dt, int G, int M, int N, int K_total,
+                                      const void* A, const void* SFA,
+                                      const void* B, const void* SFB,
+                                      mgg_sf_fmt sf,
+                                      float* D, const int32_t* psum, int accumulate,
+                                      hipStream_t stream);
 
 /* Human-readable text for a status code (static storage). */
 const char* mgg_status_string(mgg_status s);

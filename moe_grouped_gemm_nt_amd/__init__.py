@@ -11,7 +11,10 @@ Entry points (same names as the C functions):
                         expected_m=0)
     grouped_gemm_contiguous(A, B, D, m_indices, SFA=None, SFB=None, sfb_gran="block128",
                             expected_m=0)
-    grouped_gemm_kgrouped(A, B, D, ks, M, N, SFA=None, SFB=None, accumulate=True)
+    grouped_gemm_contiguous_psum(A, B, D, psum, SFA=None, SFB=None, sfb_gran="block128",
+                                 expected_m=0)
+    grouped_gemm_kgrouped(A, B, D, ks, M, N, SFA=None, SFB=None, accumulate=True,
+                          psum=False)   (psum=True calls grouped_gemm_kgrouped_psum)
 
 Element types: bfloat16 tensors select BF16; uint8 (or float8_e4m3fn) tensors select
 FP8 E4M3. Scale tensors: float32 selects FP32 scales, uint8 selects UE8M0 scales.
@@ -25,6 +28,7 @@ import os
 __all__ = [
     "grouped_gemm_masked",
     "grouped_gemm_contiguous",
+    "grouped_gemm_contiguous_psum",
     "grouped_gemm_kgrouped",
     "library_path",
     "load_library",
@@ -66,9 +70,13 @@ def load_library() -> ctypes.CDLL:
     lib.grouped_gemm_masked.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, i32,
                                         vp, vp, i32, st]
     lib.grouped_gemm_contiguous.argtypes = list(lib.grouped_gemm_masked.argtypes)
+    lib.grouped_gemm_contiguous_psum.argtypes = list(lib.grouped_gemm_masked.argtypes)
     lib.grouped_gemm_kgrouped.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, vp,
                                           vp, i32, st]
-    for f in (lib.grouped_gemm_masked, lib.grouped_gemm_contiguous, lib.grouped_gemm_kgrouped):
+    lib.grouped_gemm_kgrouped_psum.argtypes = list(lib.grouped_gemm_kgrouped.argtypes)
+    for f in (lib.grouped_gemm_masked, lib.grouped_gemm_contiguous,
+              lib.grouped_gemm_contiguous_psum, lib.grouped_gemm_kgrouped,
+              lib.grouped_gemm_kgrouped_psum):
         f.restype = ctypes.c_int
     lib.mgg_status_string.argtypes = [ctypes.c_int]
     lib.mgg_status_string.restype = ctypes.c_char_p
@@ -175,9 +183,35 @@ def grouped_gemm_contiguous(A, B, D, m_indices, SFA=None, SFB=None, sfb_gran="bl
     return D
 
 
-def grouped_gemm_kgrouped(A, B, D, ks, M, N, SFA=None, SFB=None, accumulate=True):
+def grouped_gemm_contiguous_psum(A, B, D, psum, SFA=None, SFB=None, sfb_gran="block128",
+                                 expected_m=0):
+    """D[r, :] = A[r, :] @ B[e].T for r in expert e's row segment [psum[e-1], psum[e])
+    (ends clamped to [0, M] and made non-decreasing); A[M, K], B[G, N, K], D bf16 [M, N],
+    psum int32 [G] on the device."""
+    import torch
+    lib = load_library()
+    _same_device(A, B, D, psum, SFA, SFB)
+    _contig(A, B, D, psum, SFA, SFB)
+    M, K = A.shape
+    G, N, _ = B.shape
+    _require(B.shape[2] == K, "B must be [G, N, K]")
+    _require(tuple(D.shape) == (M, N) and D.dtype == torch.bfloat16, "D must be bf16 [M, N]")
+    _require(psum.dtype == torch.int32 and psum.numel() == G, "psum must be int32 [G]")
+    dt = _elem_dtype(A)
+    _require(_elem_dtype(B) == dt, "A and B must have the same element type")
+    with torch.cuda.device(A.device):
+        _check(lib.grouped_gemm_contiguous_psum(dt, G, M, N, K, _ptr(A), _ptr(SFA), _ptr(B),
+                                                _ptr(SFB), _sf_fmt(SFA), _GRAN[sfb_gran],
+                                                _ptr(D), _ptr(psum), int(expected_m),
+                                                _stream(A.device)))
+    return D
+
+
+def grouped_gemm_kgrouped(A, B, D, ks, M, N, SFA=None, SFB=None, accumulate=True,
+                          psum=False):
     """D[e] (+)= A_e @ B_e.T over expert e's ks[e] tokens; A, B flat packed buffers
-    (expert blocks [M][k_e] / [N][k_e]), D fp32 [G, M, N], ks int32 [G] on the device."""
+    (expert blocks [M][k_e] / [N][k_e]), D fp32 [G, M, N], ks int32 [G] on the device.
+    With psum=True, ks holds cumulative token ends (k_e = ks[e] - ks[e-1])."""
     import torch
     lib = load_library()
     _same_device(A, B, D, ks, SFA, SFB)
@@ -191,7 +225,7 @@ def grouped_gemm_kgrouped(A, B, D, ks, M, N, SFA=None, SFB=None, accumulate=True
     dt = _elem_dtype(A)
     _require(_elem_dtype(B) == dt, "A and B must have the same element type")
     with torch.cuda.device(A.device):
-        _check(lib.grouped_gemm_kgrouped(dt, G, M, N, K_total, _ptr(A), _ptr(SFA), _ptr(B),
-                                         _ptr(SFB), _sf_fmt(SFA), _ptr(D), _ptr(ks),
-                                         1 if accumulate else 0, _stream(A.device)))
+        fn = lib.grouped_gemm_kgrouped_psum if psum else lib.grouped_gemm_kgrouped
+        _check(fn(dt, G, M, N, K_total, _ptr(A), _ptr(SFA), _ptr(B), _ptr(SFB), _sf_fmt(SFA),
+                  _ptr(D), _ptr(ks), 1 if accumulate else 0, _stream(A.device)))
     return D

@@ -43,7 +43,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-enum Variant { kMasked = 0, kContig = 1, kKGrouped = 2 };
+enum Variant { kMasked = 0, kContig = 1, kKGrouped = 2, kPsum = 3 };
 enum DType { kBF16 = 0, kFP8 = 1 };
 enum SfFmt { kSfF32 = 0, kSfUE8M0 = 1 };
 enum SfbGran { kSfbBlock = 0, kSfbChannel = 1 };
@@ -73,6 +73,7 @@ struct Params {
   int K;        // masked, contiguous: K; K-grouped: K_total
   int accumulate;  // K-grouped: 1 adds the product to D
   int k_granule;   // K-grouped: required multiple of k_e (128 FP8, 8 BF16)
+  int meta_psum;   // K-grouped: the routing holds cumulative token ends, not counts
   uint32_t sfa_bytes, sfb_bytes;  // readable bytes of the scale tensors (FP8)
   uint32_t meta_bytes;            // bytes of the routing tensor
 };
@@ -122,6 +123,37 @@ __device__ __forceinline__ float load_scale(const void* base, long idx) {
   } else {
     return ue8m0_to_float(reinterpret_cast<const uint8_t*>(base)[idx]);
   }
+}
+
+// Inclusive running maximum of `n` ints held in LDS `buf` (in place), block-wide over NT
+// threads; same structure as the scan below (every thread must call it, `s_tmp` needs
+// NT / 64 ints, two barriers).
+template <int NT>
+__device__ void block_inclusive_max(int* buf, int n, int* s_tmp) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (n + NT - 1) / NT;
+  const int lo = tid * per;
+  const int hi = min(lo + per, n);
+  int local = INT_MIN;
+  for (int i = lo; i < hi; ++i) local = max(local, buf[i]);
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl = max(incl, v);
+  }
+  if (lane == 63) s_tmp[wave] = incl;
+  __syncthreads();
+  int run = INT_MIN;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) run = w < wave ? max(run, s_tmp[w]) : run;
+  const int before_lane = __shfl_up(incl, 1, 64);
+  if (lane > 0) run = max(run, before_lane);  // maximum of everything before this chunk
+  for (int i = lo; i < hi; ++i) {
+    run = max(run, buf[i]);
+    buf[i] = run;
+  }
+  __syncthreads();
 }
 
 // Exclusive scan of `n` ints held in LDS `buf` (in place), block-wide over NT threads;

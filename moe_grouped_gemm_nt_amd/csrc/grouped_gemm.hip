@@ -73,7 +73,7 @@ void sched_bytes(const Params& p, long* persistent, long* transient) {
     *persistent = nb * 4;
     *transient = (kThreads + nb) * 4;
   } else {
-    *persistent = 2L * p.G * 4;
+    *persistent = (VAR == kPsum ? 3L : 2L) * p.G * 4;
     *transient = kThreads * 4;
   }
 }
@@ -130,6 +130,7 @@ template <class T, int VAR>
 long m_tiles(const Params& p) {
   const long ntn = cdiv(p.N, T::BN);
   if (VAR == kMasked) return (long)p.G * cdiv(p.rows, T::BM) * ntn;
+  if (VAR == kPsum) return (cdiv(p.rows, T::BM) + p.G) * ntn;  // one ragged tile per expert
   return cdiv(p.rows, kContigBlock) * (kContigBlock / T::BM) * ntn;
 }
 
@@ -205,6 +206,13 @@ mgg_status check_sizes(std::initializer_list<long> sizes) {
   return MGG_OK;
 }
 
+}  // namespace
+
+namespace {
+mgg_status kgrouped_impl(mgg_dtype dt, int G, int M, int N, int K_total, const void* A,
+                         const void* SFA, const void* B, const void* SFB, mgg_sf_fmt sf,
+                         float* D, const int32_t* ks, int accumulate, int meta_psum,
+                         hipStream_t stream);
 }  // namespace
 
 extern "C" {
@@ -290,10 +298,64 @@ mgg_status grouped_gemm_contiguous(mgg_dtype dt, int G, int M, int N, int K, con
   return dispatch_m<kContig>(dt, sf, gran, pick_tile(expected_m, kContigBlock), p, stream);
 }
 
+mgg_status grouped_gemm_contiguous_psum(mgg_dtype dt, int G, int M, int N, int K,
+                                        const void* A, const void* SFA, const void* B,
+                                        const void* SFB, mgg_sf_fmt sf, mgg_sfb_gran gran,
+                                        void* D, const int32_t* psum, int expected_m,
+                                        hipStream_t stream) {
+  g_last_error.clear();
+  mgg_status st = check_common(dt, N, K, A, SFA, B, SFB, sf, D, psum);
+  if (st != MGG_OK) return st;
+  if (G < 1 || G > kMaxExperts) return fail(MGG_EINVAL, "G must be in [1, 4096]");
+  if (M < 1) return fail(MGG_EINVAL, "M must be positive");
+  if (dt == MGG_FP8_E4M3 && gran != MGG_SFB_BLOCK128 && gran != MGG_SFB_CHANNEL)
+    return fail(MGG_EINVAL, "unknown weight-scale granularity");
+  const long esz = dt == MGG_FP8_E4M3 ? 1 : 2, KB = K / 128, NB = cdiv(N, 128);
+  const long sfa_n = KB * M;
+  const long sfb_n = gran == MGG_SFB_BLOCK128 ? (long)G * NB * KB : (long)G * KB * N;
+  st = check_sizes({(long)M * K * esz, (long)N * K * esz, (long)M * N * 2, sfa_n * 4, sfb_n * 4,
+                    (cdiv(M, 32) + G) * cdiv(N, 64)});
+  if (st != MGG_OK) return st;
+  Params p{};
+  p.A = (const uint8_t*)A;
+  p.B = (const uint8_t*)B;
+  p.SFA = SFA;
+  p.SFB = SFB;
+  p.D = D;
+  p.meta = psum;
+  p.G = G;
+  p.rows = M;
+  p.N = N;
+  p.K = K;
+  p.sfa_bytes = dt == MGG_FP8_E4M3 ? scale_bytes(sfa_n, sf) : 0;
+  p.sfb_bytes = dt == MGG_FP8_E4M3 ? scale_bytes(sfb_n, sf) : 0;
+  p.meta_bytes = (uint32_t)G * 4;
+  return dispatch_m<kPsum>(dt, sf, gran, pick_tile(expected_m, kContigBlock), p, stream);
+}
+
 mgg_status grouped_gemm_kgrouped(mgg_dtype dt, int G, int M, int N, int K_total, const void* A,
                                  const void* SFA, const void* B, const void* SFB,
                                  mgg_sf_fmt sf, float* D, const int32_t* ks, int accumulate,
                                  hipStream_t stream) {
+  return kgrouped_impl(dt, G, M, N, K_total, A, SFA, B, SFB, sf, D, ks, accumulate, 0, stream);
+}
+
+mgg_status grouped_gemm_kgrouped_psum(mgg_dtype dt, int G, int M, int N, int K_total,
+                                      const void* A, const void* SFA, const void* B,
+                                      const void* SFB, mgg_sf_fmt sf, float* D,
+                                      const int32_t* psum, int accumulate, hipStream_t stream) {
+  return kgrouped_impl(dt, G, M, N, K_total, A, SFA, B, SFB, sf, D, psum, accumulate, 1, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// K-grouped call; `meta_psum` selects cumulative token ends instead of per-expert counts.
+mgg_status kgrouped_impl(mgg_dtype dt, int G, int M, int N, int K_total, const void* A,
+                         const void* SFA, const void* B, const void* SFB, mgg_sf_fmt sf,
+                         float* D, const int32_t* ks, int accumulate, int meta_psum,
+                         hipStream_t stream) {
   g_last_error.clear();
   if (K_total < 0) return fail(MGG_EINVAL, "K_total must be non-negative");
   // check_common wants K >= 1; an empty token axis is still a valid call.
@@ -321,6 +383,7 @@ mgg_status grouped_gemm_kgrouped(mgg_dtype dt, int G, int M, int N, int K_total,
   p.K = K_total;
   p.accumulate = accumulate;
   p.k_granule = dt == MGG_FP8_E4M3 ? 128 : 8;
+  p.meta_psum = meta_psum;
   p.sfa_bytes = dt == MGG_FP8_E4M3 ? scale_bytes(KB * M, sf) : 0;
   p.sfb_bytes = dt == MGG_FP8_E4M3 ? scale_bytes(KB * N, sf) : 0;
   p.meta_bytes = (uint32_t)G * 4;
@@ -333,4 +396,4 @@ mgg_status grouped_gemm_kgrouped(mgg_dtype dt, int G, int M, int N, int K_total,
 #undef MGG_KG
 }
 
-}  // extern "C"
+}  // namespace

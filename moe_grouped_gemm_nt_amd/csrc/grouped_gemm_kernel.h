@@ -53,8 +53,9 @@ struct TileCtx {
 template <class T, int VAR>
 struct Sched {
   int* s_a;    // masked: tile prefix [G]; K-grouped: p_e [G]
-  int* s_b;    // masked: clamped counts [G]; contiguous: packed (block << 12 | expert) of
-               // each valid block; K-grouped: usable k_e or -1 [G]
+  int* s_b;    // masked, psum: row counts [G]; contiguous: packed (block << 12 | expert)
+               // of each valid block; K-grouped: usable k_e or -1 [G]
+  int* s_c;    // psum: first row of each expert's segment [G]
   int total;   // number of tiles
   int ntn;     // n tiles per expert
   int mtn;     // K-grouped: m tiles per expert
@@ -130,6 +131,38 @@ __device__ __forceinline__ void sched_init(Sched<T, VAR>& S, const Params& p, in
     }
     __syncthreads();
     S.total = block_exclusive_scan<NT>(S.s_a, p.G, s_tmp);
+  } else if constexpr (VAR == kPsum) {
+    // Expert g owns rows [start_g, end_g): end_g = clamp(psum[g], 0, M) raised to the
+    // running maximum of the earlier ends, start_g = end_{g-1} (0 for g = 0), so the
+    // segments never overlap whatever the routing holds.
+    for (int g = tid; g < p.G; g += NT) {
+      int e = p.meta[g];
+      S.s_c[g] = e < 0 ? 0 : (e > p.rows ? p.rows : e);
+    }
+    __syncthreads();
+    block_inclusive_max<NT>(S.s_c, p.G, s_tmp);  // s_c[g] = end_g
+    int st0[8], cnt[8];  // this thread's experts (G <= 8 * NT)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int g = tid + q * NT;
+      st0[q] = cnt[q] = 0;
+      if (g < p.G) {
+        st0[q] = g > 0 ? S.s_c[g - 1] : 0;
+        cnt[q] = S.s_c[g] - st0[q];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int g = tid + q * NT;
+      if (g < p.G) {
+        S.s_c[g] = st0[q];
+        S.s_b[g] = cnt[q];
+        S.s_a[g] = ((cnt[q] + T::BM - 1) / T::BM) * S.ntn;
+      }
+    }
+    __syncthreads();
+    S.total = block_exclusive_scan<NT>(S.s_a, p.G, s_tmp);
   } else if constexpr (VAR == kContig) {
     // s_flag (transient, inside the pipeline stages) holds the block flags and then
     // their prefix; valid blocks are packed into s_b in block order.
@@ -149,7 +182,7 @@ __device__ __forceinline__ void sched_init(Sched<T, VAR>& S, const Params& p, in
   } else {
     S.mtn = (p.rows + T::BM - 1) / T::BM;
     for (int g = tid; g < p.G; g += NT) {
-      const int k = p.meta[g];
+      const int k = p.meta_psum ? p.meta[g] - (g > 0 ? p.meta[g - 1] : 0) : p.meta[g];
       S.s_b[g] = k;
       S.s_a[g] = k > 0 ? k : 0;
     }
@@ -184,7 +217,7 @@ template <class T, int VAR, int DT, int GRAN>
 __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Params& p, long& L) {
   TileCtx t = {};  // valid == 0, null bases: an idle cursor copies nothing
   constexpr int esz = DT == kFP8 ? 1 : 2;
-  if constexpr (VAR == kMasked) {
+  if constexpr (VAR == kMasked || VAR == kPsum) {
     if (L < S.total) {
       int lo = 0, hi = p.G - 1;  // largest g with prefix[g] <= L
       while (lo < hi) {
@@ -206,12 +239,15 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       t.nk = (Kb + kSliceBytes - 1) / kSliceBytes;
       t.a_lim = c;
       t.row_end = c;
-      t.a_base = p.A + (long)g * p.rows * Kb;
-      t.a_bytes = (uint32_t)((long)p.rows * Kb);
+      // masked: expert g's block of cap rows; psum: its segment of the [M] rows
+      const long r0 = VAR == kPsum ? (long)S.s_c[g] : (long)g * p.rows;
+      const long rn = VAR == kPsum ? (long)c : (long)p.rows;
+      t.a_base = p.A + r0 * Kb;
+      t.a_bytes = (uint32_t)(rn * Kb);
       t.b_base = p.B + (long)g * p.N * Kb;
       t.b_bytes = (uint32_t)((long)p.N * Kb);
       t.lda = t.ldb = Kb;
-      t.sfa_off = (long)g * KB * p.rows;
+      t.sfa_off = VAR == kPsum ? r0 : (long)g * KB * p.rows;
       t.sfa_ld = p.rows;
       if constexpr (GRAN == kSfbBlock) {
         t.sfb_off = (long)g * ((p.N + 127) / 128) * KB;
@@ -220,8 +256,8 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
         t.sfb_off = (long)g * KB * p.N;
         t.sfb_ld = p.N;
       }
-      t.d_base = reinterpret_cast<uint8_t*>(p.D) + (long)g * p.rows * p.N * 2;
-      t.d_bytes = (uint32_t)((long)p.rows * p.N * 2);
+      t.d_base = reinterpret_cast<uint8_t*>(p.D) + r0 * p.N * 2;
+      t.d_bytes = (uint32_t)(rn * p.N * 2);
     }
   } else if constexpr (VAR == kContig) {
     constexpr int SUB = kContigBlock / T::BM;
@@ -408,6 +444,7 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
     const int n = (VAR == kContig) ? (p.rows + kContigBlock - 1) / kContigBlock : p.G;
     Sd.s_a = base;
     Sd.s_b = base + (VAR == kContig ? 0 : n);
+    Sd.s_c = base + 2 * n;
     int* s_tmp = reinterpret_cast<int*>(smem);
     int* s_flag = s_tmp + kThreads;
     sched_init<T, VAR, Lay::NT>(Sd, p, s_tmp, s_flag);

@@ -164,6 +164,7 @@ class Problem:
     counts: torch.Tensor | None = None  # masked, int32 [G]
     m_indices: torch.Tensor | None = None  # contiguous, int32 [M]
     ks: torch.Tensor | None = None  # K-grouped, int32 [G]
+    psum: torch.Tensor | None = None  # prefix-sum routing, int32 [G]
     K_total: int = 0
     meta: dict = field(default_factory=dict)
 
@@ -172,7 +173,7 @@ class Problem:
         if self.variant == "masked":
             c = np.clip(self.meta["counts"], 0, self.cap)
             return float(2 * int(c.sum()) * self.N * self.K)
-        if self.variant == "contiguous":
+        if self.variant in ("contiguous", "psum"):
             return float(2 * int(self.meta["valid_rows"]) * self.N * self.K)
         return float(2 * self.M * self.N * int(np.sum(self.meta["ks"])))
 
@@ -256,6 +257,27 @@ def make_contiguous(dtype: str, G: int, N: int, K: int, seg_counts, seed: int,
                    m_indices=torch.tensor(idx, dtype=torch.int32, device=device),
                    meta={"seg_counts": np.asarray(seg_counts, np.int64),
                          "m_indices": idx, "valid_rows": valid_rows, "seed": seed})
+
+
+def make_contiguous_psum(dtype: str, G: int, N: int, K: int, seg_counts, seed: int,
+                         device="cpu", sf_fmt="f32", sfb_gran="block128", tail=0,
+                         std_a=1.0, std_b=1.0) -> Problem:
+    """Prefix-sum routed contiguous problem: expert segments back to back with no
+    alignment, then `tail` unrouted rows; psum[e] = rows of experts 0..e."""
+    seg = np.asarray(seg_counts, np.int64)
+    psum = np.cumsum(seg).astype(np.int32)
+    M = int(seg.sum()) + int(tail)
+    gen = _gen(seed, device)
+    a = randn((M, K), 0, device, std_a, gen=gen)
+    if dtype == "bf16":
+        A, SFA = a, None
+    else:
+        A, SFA = quant_rows_1x128(a, sf_fmt)
+    B, SFB = _weights(dtype, G, N, K, gen, device, sf_fmt, sfb_gran, std_b)
+    return Problem("psum", dtype, G, N, K, A, B, SFA, SFB, sf_fmt, sfb_gran, M=M,
+                   psum=torch.tensor(psum, dtype=torch.int32, device=device),
+                   meta={"seg_counts": seg, "psum": psum, "valid_rows": int(seg.sum()),
+                         "seed": seed})
 
 
 def make_kgrouped(dtype: str, ks, M: int, N: int, seed: int, device="cpu",

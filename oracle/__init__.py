@@ -11,6 +11,9 @@ Parity status of each function (what pins it lives in tests/test_oracle_*.py):
   grouped_gemm_masked / _contiguous / _kgrouped               pinned (brute force with
       exact rationals, integer-exact cases, one-hot weights, cross-variant identities,
       the zero-channel exact zero, the printed reference norm of the K-grouped repro)
+  grouped_gemm_contiguous_psum, psum_segments,
+  kgrouped_ks_from_psum                                       pinned (literal segment
+      cases, equality with the masked oracle per segment, exact-rational brute force)
   calc_diff                                                   pinned (closed forms)
 """
 
@@ -30,8 +33,11 @@ from .grouped_gemm import (  # noqa: F401
     dequant_weight_rows,
     gemm_nt_fp64,
     grouped_gemm_contiguous,
+    grouped_gemm_contiguous_psum,
     grouped_gemm_kgrouped,
     grouped_gemm_masked,
     kgrouped_layout,
+    kgrouped_ks_from_psum,
+    psum_segments,
     valid_counts,
 )

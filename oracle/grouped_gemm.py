@@ -17,6 +17,9 @@ What is computed, and where it is defined:
   analysis comment): rows of all experts are concatenated and a per-row expert index
   (`m_indices`) routes each row to its expert's weight; scales are 1x128 per token group
   on activations and 128x128 blocks on weights, possibly powers of two.
+* The prefix-sum ("psum") routing of the contiguous and K-grouped GEMMs, named on the
+  pages without a description (see psum_segments and kgrouped_ks_from_psum for the
+  reading taken).
 * The K-grouped weight-gradient GEMM of the DeepGEMM issue "Non-deterministic numerical
   problem of k_grouped_fp8_gemm_nt_contiguous" (section "repro script"): expert e owns
   k_e consecutive tokens; both operands are packed per expert as [channels][k_e] blocks
@@ -177,6 +180,61 @@ def grouped_gemm_contiguous(dtype, A, B, m_indices, SFA=None, SFB=None,
                                     None if SFB is None else np.asarray(SFB)[g], sfb_gran, sf_fmt)
         ref[np.ix_(r, cols)] = gemm_nt_fp64(a_hat, b_hat)
     return ref, valid
+
+
+def psum_segments(psum, M: int):
+    """Row segment [start_e, end_e) of each expert in the prefix-sum ("psum") routing of
+    the contiguous GEMM. The pages name this mode (the use_psum_layout argument in the
+    repro script of the K-grouped issue; the psum mode of the graph-mutation test in the
+    SM120 issue's verification comment) without describing it. Reading: psum[e] is the
+    cumulative end row of expert e; each end is clamped to [0, M] and raised to the
+    largest earlier end, and expert e starts where expert e - 1 ends (row 0 for e = 0),
+    so segments are consecutive and never overlap."""
+    out = []
+    end_prev = 0
+    for v in np.asarray(psum, dtype=np.int64):
+        end = max(end_prev, min(max(int(v), 0), M))
+        out.append((end_prev, end))
+        end_prev = end
+    return out
+
+
+def grouped_gemm_contiguous_psum(dtype, A, B, psum, SFA=None, SFB=None,
+                                 sfb_gran="block128", sf_fmt="f32", cols=None):
+    """Contiguous M-grouped NT GEMM with prefix-sum routing, float64 result.
+
+    A[M, K] codes; B[G, N, K] codes; psum[G]. FP8 scales: SFA[K/128, M]; SFB per expert
+    as in the masked variant. Rows of expert e's segment (psum_segments) are
+    D[r, :] = A[r, :] . B[e]^T; rows outside every segment are not computed.
+
+    Returns (ref[M, N] float64 with NaN outside the segments, valid[M] bool).
+    """
+    A = np.asarray(A)
+    B = np.asarray(B)
+    M, K = A.shape
+    G, N, _ = B.shape
+    ref = np.full((M, N), np.nan)
+    valid = np.zeros(M, bool)
+    cols = np.arange(N) if cols is None else np.asarray(cols)
+    for e, (r0, r1) in enumerate(psum_segments(psum, M)):
+        if r1 <= r0:
+            continue
+        valid[r0:r1] = True
+        a_hat = dequant_act_rows(dtype, A[r0:r1],
+                                 None if SFA is None else np.asarray(SFA)[:, r0:r1], sf_fmt)
+        b_hat = dequant_weight_rows(dtype, B[e][cols], cols,
+                                    None if SFB is None else np.asarray(SFB)[e], sfb_gran, sf_fmt)
+        ref[np.ix_(np.arange(r0, r1), cols)] = gemm_nt_fp64(a_hat, b_hat)
+    return ref, valid
+
+
+def kgrouped_ks_from_psum(psum):
+    """Per-expert token counts of the K-grouped call's prefix-sum routing (its
+    use_psum_layout argument, not described on the pages): psum[e] is the cumulative
+    token end of expert e, so k_e = psum[e] - psum[e - 1] with psum[-1] = 0; a
+    decreasing entry gives a negative count, which is out of contract."""
+    ps = np.asarray(psum, dtype=np.int64)
+    return np.diff(np.concatenate([[0], ps]))
 
 
 def kgrouped_layout(ks, K_total: int, granule: int):

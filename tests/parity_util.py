@@ -231,3 +231,35 @@ def check_kgrouped(p: synth.Problem, D: torch.Tensor, C=None, experts=None, rows
         all_ref.append(r.ravel())
     diff = oracle.calc_diff(np.concatenate(all_gpu), np.concatenate(all_ref))
     return {"calc_diff": diff, "n_bad": n_bad, "worst": worst, "stray": 0, "ref": ref}
+
+
+# ----------------------------------------------------------------------------- prefix sums
+
+
+def run_psum(p: synth.Problem, expected_m=0, D=None, psum=None):
+    import moe_grouped_gemm_nt_amd as mgg
+    if D is None:
+        D = sentinel_like((p.M, p.N), p.A.device)
+    mgg.grouped_gemm_contiguous_psum(p.A, p.B, D, p.psum if psum is None else psum, p.SFA,
+                                     p.SFB, p.sfb_gran, expected_m)
+    return D
+
+
+def check_psum(p: synth.Problem, D: torch.Tensor, psum=None, check_sentinel=True):
+    """D against the prefix-sum oracle on every row of every segment; every row outside
+    the segments must keep the sentinel."""
+    Dh = bf16_bits(D)
+    ps = p.meta["psum"] if psum is None else np.asarray(psum)
+    A, B = np_codes(p.A), np_codes(p.B)
+    SFA = None if p.SFA is None else np_codes(p.SFA)
+    SFB = None if p.SFB is None else np_codes(p.SFB)
+    ref, valid = oracle.grouped_gemm_contiguous_psum(p.dtype, A, B, ps, SFA, SFB, p.sfb_gran,
+                                                     p.sf_fmt)
+    S, _ = oracle.grouped_gemm_contiguous_psum(p.dtype, abs_codes(A, p.dtype),
+                                               abs_codes(B, p.dtype), ps, SFA, SFB, p.sfb_gran,
+                                               p.sf_fmt)
+    gpu = oracle.decode_bf16(Dh[valid])
+    nb, w = elementwise_ok(gpu, ref[valid], S[valid], p.K, rounded=True, fp8=p.dtype == "fp8")
+    diff = oracle.calc_diff(gpu, oracle.decode_bf16(oracle.round_to_bf16(ref[valid])))
+    stray = int((Dh[~valid] != SENTINEL).sum()) if check_sentinel else 0
+    return {"calc_diff": diff, "n_bad": nb, "worst": w, "stray": stray}

@@ -33,12 +33,13 @@ def lib():
     return mgg.load_library()
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
-    for f in ("grouped_gemm_masked", "grouped_gemm_contiguous", "grouped_gemm_kgrouped",
-              "mgg_status_string", "mgg_last_error"):
+    for f in ("grouped_gemm_masked", "grouped_gemm_contiguous", "grouped_gemm_contiguous_psum",
+              "grouped_gemm_kgrouped", "grouped_gemm_kgrouped_psum", "mgg_status_string",
+              "mgg_last_error"):
         assert f in names
-    assert len(names) == 5, names
+    assert len(names) == 7, names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -70,6 +71,17 @@ def contig(lib, dt=1, G=2, M=256, N=16, K=128, A=P, SFA=P, B=P, SFB=P, sf=0, gra
 
 def kgrp(lib, dt=1, G=2, M=16, N=16, KT=256, A=P, SFA=P, B=P, SFB=P, sf=0, D=P, ks=P, acc=1):
     return lib.grouped_gemm_kgrouped(dt, G, M, N, KT, A, SFA, B, SFB, sf, D, ks, acc, None)
+
+
+def psum_contig(lib, dt=1, G=2, M=256, N=16, K=128, A=P, SFA=P, B=P, SFB=P, sf=0, gran=0, D=P,
+                ps=P, em=0):
+    return lib.grouped_gemm_contiguous_psum(dt, G, M, N, K, A, SFA, B, SFB, sf, gran, D, ps, em,
+                                            None)
+
+
+def kgrp_psum(lib, dt=1, G=2, M=16, N=16, KT=256, A=P, SFA=P, B=P, SFB=P, sf=0, D=P, ps=P,
+              acc=1):
+    return lib.grouped_gemm_kgrouped_psum(dt, G, M, N, KT, A, SFA, B, SFB, sf, D, ps, acc, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -139,3 +151,37 @@ def test_product_path_does_not_import_the_oracle():
             text = open(path).read()
             assert "import oracle" not in text and "from oracle" not in text, path
             assert "oracle/" not in text, path
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), EINVAL),
+    (dict(G=0), EINVAL),
+    (dict(G=4097), EINVAL),
+    (dict(M=0), EINVAL),
+    (dict(N=12), EINVAL),
+    (dict(K=100), EINVAL),
+    (dict(dt=0, K=12), EINVAL),
+    (dict(A=NUL), EINVAL),
+    (dict(ps=NUL), EINVAL),
+    (dict(SFA=NUL), EINVAL),
+    (dict(A=MIS), EINVAL),
+    (dict(ps=ctypes.c_void_p((1 << 20) + 2)), EINVAL),
+    (dict(sf=5), EINVAL),
+    (dict(gran=9), EINVAL),
+])
+def test_contiguous_psum_rejects(lib, kw, code):
+    assert psum_contig(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=7), EINVAL),
+    (dict(G=0), EINVAL),
+    (dict(M=0), EINVAL),
+    (dict(KT=-1), EINVAL),
+    (dict(KT=200), EINVAL),
+    (dict(ps=NUL), EINVAL),
+    (dict(acc=2), EINVAL),
+    (dict(D=MIS), EINVAL),
+])
+def test_kgrouped_psum_rejects(lib, kw, code):
+    assert kgrp_psum(lib, **kw) == code

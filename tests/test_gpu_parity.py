@@ -13,7 +13,8 @@ import torch
 import oracle
 from moe_grouped_gemm_nt_amd import synth
 from parity_util import (SENTINEL, assert_report, bf16_bits, check_contiguous, check_kgrouped,
-                         check_masked, run_contiguous, run_kgrouped, run_masked, say)
+                         check_masked, check_psum, run_contiguous, run_kgrouped, run_masked,
+                         run_psum, say)
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -270,3 +271,77 @@ def test_kgrouped_ue8m0_scales():
                                           512, sa.cpu().numpy(), sb.cpu().numpy(), "ue8m0")
     assert oracle.calc_diff(Dh, ref) < 1e-3
     assert np.allclose(Dh, ref, rtol=1e-3, atol=1e-4 * np.abs(ref).max())
+
+
+# ----------------------------------------------------------------------------- prefix sums
+
+
+@pytest.mark.parametrize("dtype,sf_fmt,gran", [
+    ("bf16", "f32", "block128"),
+    ("fp8", "f32", "block128"),
+    ("fp8", "ue8m0", "channel"),
+])
+def test_psum_ragged_unaligned(dtype, sf_fmt, gran):
+    """Prefix-sum routing: unaligned segments of 130, 0, 1, 127, 45 and 300 rows back to
+    back, then 7 unrouted rows; N=264; every tile shape gives the same bits; rows outside
+    the segments keep the sentinel."""
+    segs = [130, 0, 1, 127, 45, 300]
+    say("psum", dtype, sf_fmt, gran, segs)
+    p = synth.make_contiguous_psum(dtype, len(segs), 264, 256, segs, seed=21, device=DEV,
+                                   sf_fmt=sf_fmt, sfb_gran=gran, tail=7)
+    outs = []
+    for em in (8, 64, 256):
+        say("  expected_m", em)
+        D = run_psum(p, em)
+        torch.cuda.synchronize()
+        outs.append(bf16_bits(D))
+    assert_report(check_psum(p, D), dtype)
+    assert (outs[0] == outs[1]).all() and (outs[1] == outs[2]).all(), "tile shapes disagree"
+
+
+def test_psum_routing_is_clamped():
+    """Ends beyond M, negative and decreasing entries follow the stated reading (ends
+    clamped to [0, M] and raised to the running maximum); nothing overlaps and nothing
+    outside the resulting segments is written."""
+    say("psum clamped")
+    p = synth.make_contiguous_psum("fp8", 5, 136, 256, [40, 40, 40, 40, 40], seed=22,
+                                   device=DEV)
+    for ps in ([60, 30, -5, 150, 900], [0, 0, 0, 0, 0], [-1, 200, 10, 10, 200]):
+        say("  psum", ps)
+        t = torch.tensor(ps, dtype=torch.int32, device=DEV)
+        D = run_psum(p, 64, psum=t)
+        torch.cuda.synchronize()
+        assert_report(check_psum(p, D, psum=ps), "fp8")
+
+
+def test_psum_matches_contiguous_bitwise():
+    """128-aligned segments routed by prefix sums and by per-row indices give the same
+    bits."""
+    say("psum vs m_indices")
+    segs = [128, 256, 0, 128]
+    p = synth.make_contiguous_psum("fp8", 4, 256, 512, segs, seed=23, device=DEV)
+    idx = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(segs)])
+    pc = synth.Problem("contiguous", "fp8", 4, 256, 512, p.A, p.B, p.SFA, p.SFB, M=p.M,
+                       m_indices=torch.tensor(idx, device=DEV),
+                       meta={"m_indices": idx, "valid_rows": int(sum(segs))})
+    Dp = bf16_bits(run_psum(p, 128))
+    Dc = bf16_bits(run_contiguous(pc, 128))
+    assert (Dp == Dc).all()
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "bf16"])
+def test_kgrouped_psum_matches_counts(dtype):
+    """The K-grouped call with cumulative token ends gives the same bits as with counts,
+    and matches the oracle."""
+    import moe_grouped_gemm_nt_amd as mgg
+    ks = [256, 128, 0, 128, 256]
+    say("kgrouped psum", dtype, ks)
+    p = synth.make_kgrouped(dtype, ks, 96, 200, seed=24, device=DEV)
+    ps = torch.tensor(np.cumsum(ks).astype(np.int32), device=DEV)
+    D1 = run_kgrouped(p, accumulate=False)
+    D2 = torch.full_like(D1, 7.0)
+    mgg.grouped_gemm_kgrouped(p.A, p.B, D2, ps, p.M, p.N, p.SFA, p.SFB, accumulate=False,
+                              psum=True)
+    torch.cuda.synchronize()
+    assert torch.equal(D1, D2)
+    assert_report(check_kgrouped(p, D2), dtype)

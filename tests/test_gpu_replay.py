@@ -11,8 +11,8 @@ import torch
 
 from moe_grouped_gemm_nt_amd import synth
 from parity_util import (SENTINEL, assert_report, bf16_bits, check_contiguous, check_kgrouped,
-                         check_masked, run_contiguous, run_kgrouped, run_masked, say,
-                         sentinel_like)
+                         check_masked, check_psum, run_contiguous, run_kgrouped, run_masked,
+                         run_psum, say, sentinel_like)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -126,6 +126,41 @@ def test_contiguous_graph_replay_changing_indices():
         torch.cuda.synchronize()
         assert (got == eager).all()
         assert_report(check_contiguous(p, D), "fp8")
+
+
+def test_psum_graph_replay_changing_prefix_sums():
+    """One captured prefix-sum call replayed with new routing values in the same buffer
+    (including an all-empty phase and an out-of-range one) matches the eager call and the
+    oracle every time."""
+    G, N, K = 6, 256, 256
+    rng = np.random.default_rng(9)
+    M = 1500
+    draws = [np.cumsum(rng.poisson(90, G)) for _ in range(2)]
+    draws += [np.zeros(G, int), np.array([100, 50, 3000, -7, 400, 1499]),
+              np.cumsum(rng.poisson(240, G))]
+    say("psum graph")
+    p = synth.make_contiguous_psum("fp8", G, N, K, [M // G] * G, seed=9, device=DEV,
+                                   tail=M - (M // G) * G)
+    D = sentinel_like((M, N), DEV)
+    fill = sentinel_like((M, N), DEV)
+    run_psum(p, 128, D)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_psum(p, 128, D)
+    for ph, ps in enumerate(draws):
+        ps = np.asarray(ps, np.int32)
+        say("  phase", ph, ps.tolist())
+        p.psum.copy_(torch.from_numpy(ps))
+        p.meta["psum"] = ps
+        D.copy_(fill)
+        g.replay()
+        torch.cuda.synchronize()
+        got = bf16_bits(D)
+        eager = bf16_bits(run_psum(p, 128))
+        torch.cuda.synchronize()
+        assert (got == eager).all()
+        assert_report(check_psum(p, D), "fp8")
 
 
 def test_kgrouped_graph_replay_changing_ks():

@@ -339,3 +339,67 @@ def test_calc_diff_closed_forms():
     eps = 1e-3
     want = eps ** 2 / (2 + 2 * eps + eps ** 2)
     assert abs(oracle.calc_diff(x, x * (1 + eps)) - want) < 1e-15
+
+
+# ---------------------------------------------------------------- prefix-sum routing
+
+
+def test_psum_segments_literal_cases():
+    """The reading of the prefix-sum routing, case by case (hand-written expectations)."""
+    assert oracle.psum_segments([3, 3, 10], 8) == [(0, 3), (3, 3), (3, 8)]
+    # a decreasing end is raised to the running maximum: expert 1 is empty and expert 2
+    # starts where expert 0 ended, so nothing overlaps
+    assert oracle.psum_segments([10, 5, 20], 16) == [(0, 10), (10, 10), (10, 16)]
+    assert oracle.psum_segments([-4, 2, 2], 5) == [(0, 0), (0, 2), (2, 2)]
+    assert oracle.psum_segments([0, 0], 1) == [(0, 0), (0, 0)]
+
+
+@pytest.mark.parametrize("dtype,fmt,gran", [
+    ("bf16", "f32", "block128"),
+    ("fp8", "f32", "block128"),
+    ("fp8", "ue8m0", "channel"),
+])
+def test_contiguous_psum_equals_masked_per_segment(dtype, fmt, gran):
+    """Each expert's segment, taken as a masked expert of capacity = its row count,
+    gives the same rows through the masked oracle."""
+    segs = [37, 0, 130, 1]
+    p = synth.make_contiguous_psum(dtype, 4, 20, 256, segs, seed=8, sf_fmt=fmt,
+                                   sfb_gran=gran, tail=5)
+    A, B = np_codes(p.A), np_codes(p.B)
+    SFA = None if p.SFA is None else p.SFA.numpy()
+    SFB = None if p.SFB is None else p.SFB.numpy()
+    ref, valid = oracle.grouped_gemm_contiguous_psum(dtype, A, B, p.meta["psum"], SFA, SFB,
+                                                     gran, fmt)
+    assert valid.sum() == sum(segs) and not valid[-5:].any()
+    r0 = 0
+    for e, c in enumerate(segs):
+        if c:
+            sfa_e = None if SFA is None else SFA[None, :, r0:r0 + c]
+            ref_m, _ = oracle.grouped_gemm_masked(dtype, A[None, r0:r0 + c], B[e:e + 1], [c],
+                                                  sfa_e, None if SFB is None else SFB[e:e + 1],
+                                                  gran, fmt)
+            assert (ref[r0:r0 + c] == ref_m[0]).all()
+        r0 += c
+    assert np.isnan(ref[~valid]).all()
+
+
+def test_contiguous_psum_bruteforce_exact():
+    """Exact rationals over the raw layouts (rows routed by the literal segments)."""
+    p = synth.make_contiguous_psum("fp8", 2, 3, 256, [2, 3], seed=12, tail=1)
+    A, B = np_codes(p.A), np_codes(p.B)
+    av, bv = torch_decode(A, "fp8"), torch_decode(B, "fp8")
+    SFA, SFB = p.SFA.numpy(), p.SFB.numpy()
+    ref, valid = oracle.grouped_gemm_contiguous_psum("fp8", A, B, [2, 5], SFA, SFB)
+    assert valid.tolist() == [True] * 5 + [False]
+    for r, e in [(0, 0), (1, 0), (2, 1), (3, 1), (4, 1)]:
+        for n in range(3):
+            acc = Fraction(0)
+            for k in range(256):
+                acc += (Fraction(float(av[r, k])) * Fraction(float(SFA[k // 128, r])) *
+                        Fraction(float(bv[e, n, k])) * Fraction(float(SFB[e, n // 128, k // 128])))
+            assert abs(Fraction(ref[r, n]) - acc) <= abs(acc) * Fraction(1, 2 ** 40) + Fraction(1, 2 ** 200)
+
+
+def test_kgrouped_ks_from_psum_literal():
+    assert oracle.kgrouped_ks_from_psum([256, 384, 512, 768]).tolist() == [256, 128, 128, 256]
+    assert oracle.kgrouped_ks_from_psum([128, 0, 128]).tolist() == [128, -128, 128]
