@@ -15,6 +15,9 @@ Parity status of each function (what pins it lives in tests/test_oracle_*.py):
   kgrouped_ks_from_psum                                       pinned (literal segment
       cases, equality with the masked oracle per segment, exact-rational brute force)
   calc_diff                                                   pinned (closed forms)
+  encode_e4m3_rne, ue8m0_code_at_least, quantize_rows_1x128   pinned (torch's float32 ->
+      float8_e4m3fn conversion on random values and every rounding midpoint, literal
+      power-of-two cases, closed-form groups, round-trip error bound)
 """
 
 from .formats import (  # noqa: F401
@@ -24,6 +27,11 @@ from .formats import (  # noqa: F401
     decode_scale,
     decode_ue8m0,
     round_to_bf16,
+)
+from .quantize import (  # noqa: F401
+    encode_e4m3_rne,
+    quantize_rows_1x128,
+    ue8m0_code_at_least,
 )
 from .grouped_gemm import (  # noqa: F401
     SCALE_K,
