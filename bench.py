@@ -141,6 +141,9 @@ def main():
     if args.workload == "copy_calibration":
         copy_calibration(dev, args)
         return
+    if args.workload in QUANT_WORKLOADS:
+        quant_bench(dev, args)
+        return
     mgg.load_library()
     p, opt = synth.make_workload(args.workload, dev)
     flops = p.valid_flops()
@@ -243,6 +246,80 @@ def main():
         "data": "synthetic",
         "config": cfg,
         "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+QUANT_WORKLOADS = {
+    # bf16 activations -> FP8 E4M3 codes + 1x128 float32 scales: the expected tokens of the
+    # 32-expert N=6144 configuration (32 x 192) at its hidden size 7168
+    "quant_fp8_1x128_6144x7168": (6144, 7168, "f32"),
+    "quant_fp8_1x128_ue8m0_6144x7168": (6144, 7168, "ue8m0"),
+}
+
+
+def quant_bench(dev, args):
+    """FP8 1x128 activation quantization: `steps` calls in one hipGraph, inputs rotated
+    over enough buffers to exceed the Infinity Cache; HBM roofline on the algorithmic
+    bytes (bf16 in, codes out, one scale per 128 elements)."""
+    import torch
+    import moe_grouped_gemm_nt_amd as mgg
+    mgg.load_library()
+    M, K, fmt = QUANT_WORKLOADS[args.workload]
+    sf_b = 4 if fmt == "f32" else 1
+    abytes = M * K * 2 + M * K + (K // 128) * M * sf_b
+    nrot = max(1, min(8, -(-2 * MALL_BYTES // (M * K * 3))))
+    g = torch.Generator(device=dev).manual_seed(0)
+    Xs = [torch.randn((M, K), device=dev, generator=g).to(torch.bfloat16) for _ in range(nrot)]
+    Qs = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(nrot)]
+    SFs = [torch.empty((K // 128, M), device=dev,
+                       dtype=torch.float32 if fmt == "f32" else torch.uint8) for _ in range(nrot)]
+    stream = torch.cuda.Stream(dev)
+    stream.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            mgg.quantize_fp8_1x128(Xs[i % nrot], Qs[i % nrot], SFs[i % nrot], fmt)
+    torch.cuda.synchronize(dev)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(args.steps):
+            mgg.quantize_fp8_1x128(Xs[i % nrot], Qs[i % nrot], SFs[i % nrot], fmt)
+    torch.cuda.synchronize(dev)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        t0.record(stream)
+        graph.replay()
+        t1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms_step = t0.elapsed_time(t1) / args.steps
+    gbs = abytes / (ms_step * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import oracle
+        rows = 256
+        x = Xs[0][:rows].cpu().view(torch.int16).numpy().view(np.uint16)
+        passes, t = 0, 0.0
+        w0 = time.perf_counter()
+        while t < args.cpu_seconds and passes < 10000:
+            oracle.quantize_rows_1x128(x, fmt)
+            passes += 1
+            t = time.perf_counter() - w0
+        cpu = {"value": round(rows * K * 3 * passes / t / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle", "sample": f"{rows} rows x {K} per pass; {passes} passes in {t:.1f} s"}
+    line = {
+        "metric": "FP8 1x128 activation quantization throughput (algorithmic bytes)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16->e4m3", "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "K": K, "scales": fmt,
+                   "rotating_buffers": nrot, "timing": "one hipGraph of `steps` calls"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.workload),
+                     "algorithmic_bytes_per_launch": abytes,
+                     "avg_launch_us": round(ms_step * 1e3, 3)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

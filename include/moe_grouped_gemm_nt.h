@@ -19,7 +19,8 @@
  *                            (DeepGEMM issue "Non-deterministic numerical problem of
  *                            k_grouped_fp8_gemm_nt_contiguous", section "repro script").
  * The contiguous and K-grouped products also take their routing as per-expert prefix
- * sums (the "_psum" entry points).
+ * sums (the "_psum" entry points), and quantize_fp8_1x128 produces FP8 activations with
+ * their 1x128 scales.
  *
  * Common rules for every entry point:
  *  - Every pointer is caller-owned device memory; the caller allocates every output.
@@ -184,6 +185,30 @@ mgg_status grouped_gemm_kgrouped_psum(mgg_dtype dt, int G, int M, int N, int K_t
                                       mgg_sf_fmt sf,
                                       float* D, const int32_t* psum, int accumulate,
                                       hipStream_t stream);
+
+/*
+ * FP8 E4M3 activation quantization with 1x128 per-token scales: the cast that produces
+ * the FP8 activations and their scales for the M-grouped entry points. For each row m and
+ * 128-column group kb, with float32 arithmetic throughout:
+ *   amax = max |X[m, 128 kb .. 128 kb + 127]|,  s = amax / 448
+ *   F32 scales:   s = sf_zero if s == 0; s = max(s, 1e-30); SF[kb, m] = s;
+ *                 Q[m, k] = E4M3(X[m, k] * (1 / s))
+ *   UE8M0 scales: u = smallest exponent code with 2^(u-127) >= (s == 0 ? sf_zero : s);
+ *                 SF[kb, m] = u; Q[m, k] = E4M3(X[m, k] * 2^(127-u))
+ * E4M3 conversion rounds to nearest, ties to even. This is the cast printed in the repro
+ * script of the DeepGEMM issue "Non-deterministic numerical problem of
+ * k_grouped_fp8_gemm_nt_contiguous" (there per channel over 128 tokens, with its sf_val
+ * as sf_zero), applied per token over 128 columns; the UE8M0 rounding rule is not printed
+ * on the pages (the reading taken: round the scale up to a power of two).
+ *
+ *   X    bf16 [M][K], 16-byte aligned; K a positive multiple of 128.
+ *   Q    E4M3 bytes [M][K], 8-byte aligned (may not overlap X).
+ *   SF   [K/128][M]: float32 (4-byte aligned) or one byte per scale (MGG_SF_UE8M0).
+ *   sf_zero  positive finite scale for all-zero groups.
+ * Errors: MGG_EINVAL for bad sizes, pointers, alignment, format or sf_zero.
+ */
+mgg_status quantize_fp8_1x128(int M, int K, const void* X, void* Q, void* SF, mgg_sf_fmt sf,
+                              float sf_zero, hipStream_t stream);
 
 /* Human-readable text for a status code (static storage). */
 const char* mgg_status_string(mgg_status s);

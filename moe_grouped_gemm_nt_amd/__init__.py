@@ -15,6 +15,7 @@ Entry points (same names as the C functions):
                                  expected_m=0)
     grouped_gemm_kgrouped(A, B, D, ks, M, N, SFA=None, SFB=None, accumulate=True,
                           psum=False)   (psum=True calls grouped_gemm_kgrouped_psum)
+    quantize_fp8_1x128(X, Q=None, SF=None, sf_fmt="f32", sf_zero=1.0) -> (Q, SF)
 
 Element types: bfloat16 tensors select BF16; uint8 (or float8_e4m3fn) tensors select
 FP8 E4M3. Scale tensors: float32 selects FP32 scales, uint8 selects UE8M0 scales.
@@ -30,6 +31,7 @@ __all__ = [
     "grouped_gemm_contiguous",
     "grouped_gemm_contiguous_psum",
     "grouped_gemm_kgrouped",
+    "quantize_fp8_1x128",
     "library_path",
     "load_library",
     "MggError",
@@ -74,9 +76,10 @@ def load_library() -> ctypes.CDLL:
     lib.grouped_gemm_kgrouped.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, vp,
                                           vp, i32, st]
     lib.grouped_gemm_kgrouped_psum.argtypes = list(lib.grouped_gemm_kgrouped.argtypes)
+    lib.quantize_fp8_1x128.argtypes = [i32, i32, vp, vp, vp, i32, ctypes.c_float, st]
     for f in (lib.grouped_gemm_masked, lib.grouped_gemm_contiguous,
               lib.grouped_gemm_contiguous_psum, lib.grouped_gemm_kgrouped,
-              lib.grouped_gemm_kgrouped_psum):
+              lib.grouped_gemm_kgrouped_psum, lib.quantize_fp8_1x128):
         f.restype = ctypes.c_int
     lib.mgg_status_string.argtypes = [ctypes.c_int]
     lib.mgg_status_string.restype = ctypes.c_char_p
@@ -229,3 +232,28 @@ def grouped_gemm_kgrouped(A, B, D, ks, M, N, SFA=None, SFB=None, accumulate=True
         _check(fn(dt, G, M, N, K_total, _ptr(A), _ptr(SFA), _ptr(B), _ptr(SFB), _sf_fmt(SFA),
                   _ptr(D), _ptr(ks), 1 if accumulate else 0, _stream(A.device)))
     return D
+
+
+def quantize_fp8_1x128(X, Q=None, SF=None, sf_fmt="f32", sf_zero=1.0):
+    """bf16 X[M, K] -> (Q uint8 [M, K] E4M3 codes, SF [K/128, M] float32 or uint8 UE8M0),
+    1x128 per-token scales; Q and SF are allocated when not given."""
+    import torch
+    lib = load_library()
+    _require(X.dtype == torch.bfloat16 and X.dim() == 2, "X must be bf16 [M, K]")
+    M, K = X.shape
+    if Q is None:
+        Q = torch.empty((M, K), dtype=torch.uint8, device=X.device)
+    if SF is None:
+        SF = torch.empty((K // 128, M), device=X.device,
+                         dtype=torch.float32 if sf_fmt == "f32" else torch.uint8)
+    _same_device(X, Q, SF)
+    _contig(X, Q, SF)
+    _require(tuple(Q.shape) == (M, K) and Q.dtype in (torch.uint8, torch.float8_e4m3fn),
+             "Q must be uint8 [M, K]")
+    _require(tuple(SF.shape) == (K // 128, M), "SF must be [K/128, M]")
+    fmt = {"f32": MGG_SF_F32, "ue8m0": MGG_SF_UE8M0}[sf_fmt]
+    _require((SF.dtype == torch.float32) == (fmt == MGG_SF_F32), "SF dtype must match sf_fmt")
+    with torch.cuda.device(X.device):
+        _check(lib.quantize_fp8_1x128(M, K, _ptr(X), _ptr(Q), _ptr(SF), fmt, float(sf_zero),
+                                      _stream(X.device)))
+    return Q, SF

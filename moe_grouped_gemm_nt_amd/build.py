@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB_NAME = "libmoe_grouped_gemm_nt.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["csrc/grouped_gemm.hip"]
+SOURCES = ["csrc/grouped_gemm.hip", "csrc/quantize.hip"]
 ARCH = "gfx950"
 
 

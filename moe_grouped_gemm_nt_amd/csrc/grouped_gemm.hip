@@ -229,6 +229,19 @@ const char* mgg_status_string(mgg_status s) {
 
 const char* mgg_last_error(void) { return g_last_error.c_str(); }
 
+mgg_status quantize_fp8_1x128_impl(int M, int K, const void* X, void* Q, void* SF,
+                                   mgg_sf_fmt sf, float sf_zero, hipStream_t stream,
+                                   const char** err) __attribute__((visibility("hidden")));
+
+mgg_status quantize_fp8_1x128(int M, int K, const void* X, void* Q, void* SF, mgg_sf_fmt sf,
+                              float sf_zero, hipStream_t stream) {
+  g_last_error.clear();
+  const char* err = "";
+  const mgg_status st = quantize_fp8_1x128_impl(M, K, X, Q, SF, sf, sf_zero, stream, &err);
+  if (st != MGG_OK) return fail(st, err);
+  return MGG_OK;
+}
+
 mgg_status grouped_gemm_masked(mgg_dtype dt, int G, int cap, int N, int K, const void* A,
                                const void* SFA, const void* B, const void* SFB,
                                mgg_sf_fmt sf, mgg_sfb_gran gran, void* D,

@@ -36,10 +36,10 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for f in ("grouped_gemm_masked", "grouped_gemm_contiguous", "grouped_gemm_contiguous_psum",
-              "grouped_gemm_kgrouped", "grouped_gemm_kgrouped_psum", "mgg_status_string",
-              "mgg_last_error"):
+              "grouped_gemm_kgrouped", "grouped_gemm_kgrouped_psum", "quantize_fp8_1x128",
+              "mgg_status_string", "mgg_last_error"):
         assert f in names
-    assert len(names) == 7, names
+    assert len(names) == 8, names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -185,3 +185,29 @@ def test_contiguous_psum_rejects(lib, kw, code):
 ])
 def test_kgrouped_psum_rejects(lib, kw, code):
     assert kgrp_psum(lib, **kw) == code
+
+
+def quant(lib, M=64, K=256, X=P, Q=P, SF=P, sf=0, z=1.0):
+    return lib.quantize_fp8_1x128(M, K, X, Q, SF, sf, ctypes.c_float(z), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=0), EINVAL),
+    (dict(K=0), EINVAL),
+    (dict(K=200), EINVAL),
+    (dict(X=NUL), EINVAL),
+    (dict(Q=NUL), EINVAL),
+    (dict(SF=NUL), EINVAL),
+    (dict(X=MIS), EINVAL),
+    (dict(Q=ctypes.c_void_p((1 << 20) + 4)), EINVAL),
+    (dict(SF=ctypes.c_void_p((1 << 20) + 2)), EINVAL),
+    (dict(sf=3), EINVAL),
+    (dict(z=0.0), EINVAL),
+    (dict(z=-1.0), EINVAL),
+    (dict(z=float("inf")), EINVAL),
+    (dict(z=float("nan")), EINVAL),
+    (dict(K=128 * 65536), EUNSUPPORTED),
+])
+def test_quantize_rejects(lib, kw, code):
+    assert quant(lib, **kw) == code
+    assert lib.mgg_last_error() != b""
