@@ -71,7 +71,7 @@ void sched_bytes(const Params& p, long* persistent, long* transient) {
   if (VAR == kContig) {
     const long nb = cdiv(p.rows, kContigBlock);
     *persistent = nb * 4;
-    *transient = (kThreads + nb) * 4;
+    *transient = (kThreads + 2 * nb) * 4;
   } else {
     *persistent = (VAR == kPsum ? 3L : 2L) * p.G * 4;
     *transient = kThreads * 4;

@@ -165,20 +165,33 @@ __device__ __forceinline__ void sched_init(Sched<T, VAR>& S, const Params& p, in
     S.total = block_exclusive_scan<NT>(S.s_a, p.G, s_tmp);
   } else if constexpr (VAR == kContig) {
     // s_flag (transient, inside the pipeline stages) holds the block flags and then
-    // their prefix; valid blocks are packed into s_b in block order.
+    // their prefix; s_ent (transient, after it) the block's packed entry. Valid blocks are
+    // packed into s_b in block order as (sub-tiles << 24 | block << 12 | expert), where
+    // "sub-tiles" counts the leading BM-row sub-tiles whose first row still belongs to
+    // the expert (valid rows come first in a block). Every routing value is read once,
+    // here: the tile decode reads only these tables, so every wave of the workgroup
+    // walks the same tile sequence whatever the routing buffer holds.
+    constexpr int SUB = kContigBlock / T::BM;
     const int nb = (p.rows + kContigBlock - 1) / kContigBlock;
+    int* s_ent = s_flag + nb;
     for (int b = tid; b < nb; b += NT) {
-      const int e = p.meta[(long)b * kContigBlock];
-      s_flag[b] = (e >= 0 && e < p.G) ? 1 : 0;
+      const long r0 = (long)b * kContigBlock;
+      const int e = p.meta[r0];
+      const bool ok = e >= 0 && e < p.G;
+      int nsub = ok ? 1 : 0;
+      for (int k = 1; k < SUB && nsub == k; ++k) {
+        const long r = r0 + k * T::BM;
+        if (r < p.rows && p.meta[r] == e) ++nsub;
+      }
+      s_flag[b] = ok ? 1 : 0;
+      s_ent[b] = (nsub << 24) | (b << 12) | (ok ? e : 0);
     }
     __syncthreads();
     const int nvalid = block_exclusive_scan<NT>(s_flag, nb, s_tmp);
-    for (int b = tid; b < nb; b += NT) {
-      const int e = p.meta[(long)b * kContigBlock];
-      if (e >= 0 && e < p.G) S.s_b[s_flag[b]] = (b << 12) | e;
-    }
+    for (int b = tid; b < nb; b += NT)
+      if (s_ent[b] >> 24) S.s_b[s_flag[b]] = s_ent[b];
     __syncthreads();
-    S.total = nvalid * (kContigBlock / T::BM) * S.ntn;
+    S.total = nvalid * SUB * S.ntn;
   } else {
     S.mtn = (p.rows + T::BM - 1) / T::BM;
     for (int g = tid; g < p.G; g += NT) {
@@ -266,11 +279,11 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       const long rest = L / S.ntn;
       const int sub = (int)(rest % SUB);
       const int packed = S.s_b[rest / SUB];
-      const int blk = packed >> 12, e = packed & 0xfff;
+      const int blk = (packed >> 12) & 0xfff, e = packed & 0xfff, nsub = packed >> 24;
       const int m0 = blk * kContigBlock + sub * T::BM;
       // A sub-tile that starts on padding is padding throughout (valid rows come first
       // in a block); skip it without loading anything.
-      if (m0 >= p.rows || (SUB > 1 && sub > 0 && p.meta[m0] != e)) { L += gridDim.x; continue; }
+      if (sub >= nsub || m0 >= p.rows) { L += gridDim.x; continue; }
       const int Kb = p.K * esz;
       const int KB = p.K / 128;
       t.valid = 1;
