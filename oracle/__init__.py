@@ -18,6 +18,9 @@ Parity status of each function (what pins it lives in tests/test_oracle_*.py):
   encode_e4m3_rne, ue8m0_code_at_least, quantize_rows_1x128   pinned (torch's float32 ->
       float8_e4m3fn conversion on random values and every rounding midpoint, literal
       power-of-two cases, closed-form groups, round-trip error bound)
+  exp_f32, silu_f32, swiglu_values, swiglu_quant_rows_1x128   pinned (float64 exp and
+      torch's silu within a few ulps, special values, exact cases where silu(x) = x,
+      equality with the plain quantization of exactly representable products)
 """
 
 from .formats import (  # noqa: F401
@@ -31,7 +34,14 @@ from .formats import (  # noqa: F401
 from .quantize import (  # noqa: F401
     encode_e4m3_rne,
     quantize_rows_1x128,
+    quantize_values_1x128,
     ue8m0_code_at_least,
+)
+from .swiglu import (  # noqa: F401
+    exp_f32,
+    silu_f32,
+    swiglu_quant_rows_1x128,
+    swiglu_values,
 )
 from .grouped_gemm import (  # noqa: F401
     SCALE_K,

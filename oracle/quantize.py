@@ -73,7 +73,13 @@ def quantize_rows_1x128(x_codes, sf_fmt: str = "f32", sf_zero: float = 1.0):
     SF[K/128, M]). SF is float32 (sf_fmt "f32") or UE8M0 bytes (sf_fmt "ue8m0"); an
     all-zero group takes the scale `sf_zero` (for UE8M0, the smallest power of two not
     below it)."""
-    x = decode_bf16(np.asarray(x_codes)).astype(np.float32)
+    return quantize_values_1x128(decode_bf16(np.asarray(x_codes)).astype(np.float32), sf_fmt,
+                                 sf_zero)
+
+
+def quantize_values_1x128(x, sf_fmt: str = "f32", sf_zero: float = 1.0):
+    """The same cast on float32 values X[M, K]."""
+    x = np.asarray(x, dtype=np.float32)
     M, K = x.shape
     if K % GROUP:
         raise ValueError("K must be a multiple of 128")
