@@ -210,6 +210,30 @@ mgg_status grouped_gemm_kgrouped_psum(mgg_dtype dt, int G, int M, int N, int K_t
 mgg_status quantize_fp8_1x128(int M, int K, const void* X, void* Q, void* SF, mgg_sf_fmt sf,
                               float sf_zero, hipStream_t stream);
 
+/*
+ * SwiGLU + FP8 re-quantization between an expert's gate/up GEMM (w13) and its down GEMM
+ * (w2): the step between the two contiguous FP8 GEMMs of the serving chain in the
+ * DeepGEMM issue "SM120 m_grouped_fp8 contiguous kernel: illegal memory access at CUDA
+ * graph replay" (sections "Environment" and "What works"), whose activation the pages
+ * leave unnamed (the reading taken: the gated unit silu(gate) * up). For each row m and
+ * column i < I, in float32:
+ *   x[m, i] = silu(H[m, i]) * H[m, I + i],  silu(g) = g / (1 + e^-g)
+ * with e^y one fixed evaluation (t = y log2 e; n = nearest integer to t, ties to even;
+ * degree-7 Taylor polynomial of 2^(t - n) in Horner form, every multiply and add rounded
+ * separately; scaled by 2^n; t > 128 gives +inf, t < -150 gives 0), and x is then
+ * quantized exactly as quantize_fp8_1x128 does with K = I.
+ *
+ *   H    bf16 [M][2I] (w13 output: gate columns first, then up), 16-byte aligned;
+ *        I a positive multiple of 128.
+ *   Q    E4M3 bytes [M][I], 8-byte aligned (may not overlap H).
+ *   SF   [I/128][M]: float32 (4-byte aligned) or one byte per scale (MGG_SF_UE8M0).
+ *   sf_zero  positive finite scale for all-zero groups.
+ * Every row is processed (rows a contiguous GEMM skipped hold whatever H holds there).
+ * Errors: MGG_EINVAL for bad sizes, pointers, alignment, format or sf_zero.
+ */
+mgg_status swiglu_quant_fp8_1x128(int M, int I, const void* H, void* Q, void* SF,
+                                  mgg_sf_fmt sf, float sf_zero, hipStream_t stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* mgg_status_string(mgg_status s);
 

@@ -16,6 +16,7 @@ Entry points (same names as the C functions):
     grouped_gemm_kgrouped(A, B, D, ks, M, N, SFA=None, SFB=None, accumulate=True,
                           psum=False)   (psum=True calls grouped_gemm_kgrouped_psum)
     quantize_fp8_1x128(X, Q=None, SF=None, sf_fmt="f32", sf_zero=1.0) -> (Q, SF)
+    swiglu_quant_fp8_1x128(H, Q=None, SF=None, sf_fmt="f32", sf_zero=1.0) -> (Q, SF)
 
 Element types: bfloat16 tensors select BF16; uint8 (or float8_e4m3fn) tensors select
 FP8 E4M3. Scale tensors: float32 selects FP32 scales, uint8 selects UE8M0 scales.
@@ -32,6 +33,7 @@ __all__ = [
     "grouped_gemm_contiguous_psum",
     "grouped_gemm_kgrouped",
     "quantize_fp8_1x128",
+    "swiglu_quant_fp8_1x128",
     "library_path",
     "load_library",
     "MggError",
@@ -77,9 +79,11 @@ def load_library() -> ctypes.CDLL:
                                           vp, i32, st]
     lib.grouped_gemm_kgrouped_psum.argtypes = list(lib.grouped_gemm_kgrouped.argtypes)
     lib.quantize_fp8_1x128.argtypes = [i32, i32, vp, vp, vp, i32, ctypes.c_float, st]
+    lib.swiglu_quant_fp8_1x128.argtypes = list(lib.quantize_fp8_1x128.argtypes)
     for f in (lib.grouped_gemm_masked, lib.grouped_gemm_contiguous,
               lib.grouped_gemm_contiguous_psum, lib.grouped_gemm_kgrouped,
-              lib.grouped_gemm_kgrouped_psum, lib.quantize_fp8_1x128):
+              lib.grouped_gemm_kgrouped_psum, lib.quantize_fp8_1x128,
+              lib.swiglu_quant_fp8_1x128):
         f.restype = ctypes.c_int
     lib.mgg_status_string.argtypes = [ctypes.c_int]
     lib.mgg_status_string.restype = ctypes.c_char_p
@@ -237,10 +241,25 @@ def grouped_gemm_kgrouped(A, B, D, ks, M, N, SFA=None, SFB=None, accumulate=True
 def quantize_fp8_1x128(X, Q=None, SF=None, sf_fmt="f32", sf_zero=1.0):
     """bf16 X[M, K] -> (Q uint8 [M, K] E4M3 codes, SF [K/128, M] float32 or uint8 UE8M0),
     1x128 per-token scales; Q and SF are allocated when not given."""
+    return _quant(False, X, Q, SF, sf_fmt, sf_zero)
+
+
+def swiglu_quant_fp8_1x128(H, Q=None, SF=None, sf_fmt="f32", sf_zero=1.0):
+    """bf16 w13 output H[M, 2I] (gate columns, then up) -> (Q uint8 [M, I] E4M3 codes of
+    silu(gate) * up, SF [I/128, M]); Q and SF are allocated when not given."""
+    return _quant(True, H, Q, SF, sf_fmt, sf_zero)
+
+
+def _quant(swiglu, X, Q, SF, sf_fmt, sf_zero):
     import torch
     lib = load_library()
-    _require(X.dtype == torch.bfloat16 and X.dim() == 2, "X must be bf16 [M, K]")
+    name = "H" if swiglu else "X"
+    _require(X.dtype == torch.bfloat16 and X.dim() == 2,
+             f"{name} must be bf16 [M, {'2I' if swiglu else 'K'}]")
     M, K = X.shape
+    if swiglu:
+        _require(K % 2 == 0, "H must have an even number of columns")
+        K //= 2
     if Q is None:
         Q = torch.empty((M, K), dtype=torch.uint8, device=X.device)
     if SF is None:
@@ -249,11 +268,12 @@ def quantize_fp8_1x128(X, Q=None, SF=None, sf_fmt="f32", sf_zero=1.0):
     _same_device(X, Q, SF)
     _contig(X, Q, SF)
     _require(tuple(Q.shape) == (M, K) and Q.dtype in (torch.uint8, torch.float8_e4m3fn),
-             "Q must be uint8 [M, K]")
-    _require(tuple(SF.shape) == (K // 128, M), "SF must be [K/128, M]")
+             "Q must be uint8 [M, %s]" % ("I" if swiglu else "K"))
+    _require(tuple(SF.shape) == (K // 128, M),
+             "SF must be [%s/128, M]" % ("I" if swiglu else "K"))
     fmt = {"f32": MGG_SF_F32, "ue8m0": MGG_SF_UE8M0}[sf_fmt]
     _require((SF.dtype == torch.float32) == (fmt == MGG_SF_F32), "SF dtype must match sf_fmt")
+    fn = lib.swiglu_quant_fp8_1x128 if swiglu else lib.quantize_fp8_1x128
     with torch.cuda.device(X.device):
-        _check(lib.quantize_fp8_1x128(M, K, _ptr(X), _ptr(Q), _ptr(SF), fmt, float(sf_zero),
-                                      _stream(X.device)))
+        _check(fn(M, K, _ptr(X), _ptr(Q), _ptr(SF), fmt, float(sf_zero), _stream(X.device)))
     return Q, SF

@@ -242,6 +242,19 @@ mgg_status quantize_fp8_1x128(int M, int K, const void* X, void* Q, void* SF, mg
   return MGG_OK;
 }
 
+mgg_status swiglu_quant_fp8_1x128_impl(int M, int I, const void* H, void* Q, void* SF,
+                                       mgg_sf_fmt sf, float sf_zero, hipStream_t stream,
+                                       const char** err) __attribute__((visibility("hidden")));
+
+mgg_status swiglu_quant_fp8_1x128(int M, int I, const void* H, void* Q, void* SF,
+                                  mgg_sf_fmt sf, float sf_zero, hipStream_t stream) {
+  g_last_error.clear();
+  const char* err = "";
+  const mgg_status st = swiglu_quant_fp8_1x128_impl(M, I, H, Q, SF, sf, sf_zero, stream, &err);
+  if (st != MGG_OK) return fail(st, err);
+  return MGG_OK;
+}
+
 mgg_status grouped_gemm_masked(mgg_dtype dt, int G, int cap, int N, int K, const void* A,
                                const void* SFA, const void* B, const void* SFB,
                                mgg_sf_fmt sf, mgg_sfb_gran gran, void* D,

@@ -1,6 +1,6 @@
 // quantize.hip - FP8 E4M3 activation quantization with 1x128 per-token scales, the step
 // that feeds the M-grouped GEMMs their FP8 activations (C ABI in
-// include/moe_grouped_gemm_nt.h: quantize_fp8_1x128).
+// include/moe_grouped_gemm_nt.h: quantize_fp8_1x128, swiglu_quant_fp8_1x128).
 //
 // Per row and 128-column group: amax = max |x|; scale s = amax / 448 (an all-zero group
 // takes the caller's `sf_zero`; F32 scales are floored at 1e-30), codes = E4M3(x / s)
@@ -9,13 +9,21 @@
 // k_grouped_fp8_gemm_nt_contiguous", applied along K per token. UE8M0 scales are the
 // smallest power of two not below amax / 448 (exact scaling, no code can overflow).
 //
-// Layout: X bf16 [M][K] (K contiguous), Q E4M3 bytes [M][K], SF [K/128][M] (float32 or one
-// byte per scale) — the activation-scale layout the GEMM entry points read.
+// The SwiGLU variant sits between an expert's gate/up GEMM (w13) and its down GEMM (w2)
+// (the chain of the DeepGEMM issue "SM120 m_grouped_fp8 contiguous kernel: illegal memory
+// access at CUDA graph replay", sections "Environment" and "What works"): x is
+// silu(gate) * up in float32, gate the first I columns of the bf16 w13 output and up the
+// last I, and x is quantized exactly as above.
+//
+// Layout: X bf16 [M][K] (K contiguous; [M][2K] for SwiGLU), Q E4M3 bytes [M][K],
+// SF [K/128][M] (float32 or one byte per scale) — the activation-scale layout the GEMM
+// entry points read.
 //
 // One workgroup handles 16 rows x 512 columns (see quant_rows_1x128); the group maximum
-// is a 16-lane butterfly. The kernel is HBM-bound (3 bytes per element).
+// is a 16-lane butterfly. The kernel is HBM-bound (3 bytes per element; 5 for SwiGLU).
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 #include "moe_grouped_gemm_nt.h"
@@ -45,11 +53,57 @@ __device__ __forceinline__ uint32_t to_e4m3x4(float a, float b, float c, float d
   return (uint32_t)w;
 }
 
+// Taylor coefficients (ln 2)^k / k!, k = 0..7, of 2^r = e^(r ln 2): each built in double
+// as c_k = c_(k-1) * ln 2 / k and rounded once to float.
+struct ExpPoly {
+  float c[8];
+};
+constexpr ExpPoly make_exp_poly() {
+  ExpPoly p{};
+  double c = 1.0;
+  p.c[0] = 1.0f;
+  for (int k = 1; k < 8; ++k) {
+    c = c * 0.6931471805599453 / k;
+    p.c[k] = (float)c;
+  }
+  return p;
+}
+constexpr ExpPoly kExpPoly = make_exp_poly();
+
+// e^y as one fixed float32 evaluation, so that every rounding is specified: t = y log2(e)
+// (one float multiply), n = t rounded to the nearest integer (ties to even), r = t - n
+// (exact, |r| <= 1/2), 2^r by the degree-7 Taylor polynomial in Horner form with every
+// multiply and add rounded separately (contraction into fused multiply-adds is switched
+// off here), then an exact scaling by 2^n. t is clamped to [-150, 128]: above 128 the
+// result is +inf, below -150 it is 0. Relative error below 1e-5 on the range silu uses.
+__device__ __forceinline__ float exp_fixed(float y) {
+#pragma clang fp contract(off)
+  float t = y * (float)1.4426950408889634;
+  const bool big = t > 128.0f, small = t < -150.0f;
+  t = fminf(fmaxf(t, -150.0f), 128.0f);
+  const float n = __builtin_rintf(t);
+  const float r = t - n;
+  float p = kExpPoly.c[7];
+#pragma unroll
+  for (int k = 6; k >= 0; --k) p = p * r + kExpPoly.c[k];
+  float out = ldexpf(p, (int)n);
+  out = big ? __builtin_huge_valf() : out;
+  return small ? 0.0f : out;
+}
+
+// silu(x) = x / (1 + e^-x): one float add and one IEEE float division.
+__device__ __forceinline__ float silu_fixed(float x) {
+#pragma clang fp contract(off)
+  const float d = 1.0f + exp_fixed(-x);
+  return x / d;
+}
+
 // One workgroup: 16 rows x 512 columns. Wave w takes rows 4w .. 4w + 3 of the block; in
 // each, lanes 16 g .. 16 g + 15 cover 128-column group g (8 elements per lane), so one
 // load instruction reads 1 KB of a row contiguously. The 64 scales of the block are
-// collected in LDS and written as four runs of 16 consecutive rows.
-template <bool UE8M0>
+// collected in LDS and written as four runs of 16 consecutive rows. With SWIGLU, X has
+// 2K columns per row and each lane also loads the matching up-projection columns K + col.
+template <bool UE8M0, bool SWIGLU>
 __global__ __launch_bounds__(kThreadsQ) void quant_rows_1x128(const uint16_t* __restrict__ X,
                                                               uint8_t* __restrict__ Q,
                                                               void* __restrict__ SF, int M,
@@ -61,18 +115,29 @@ __global__ __launch_bounds__(kThreadsQ) void quant_rows_1x128(const uint16_t* __
   const int kb = blockIdx.y * 4 + grp;  // this lane's 128-column group
   const bool col_ok = kb * 128 < K;     // uniform per 16-lane group
   const long col = (long)kb * 128 + l16 * 8;
-  u32x4 w[4];
+  const long ldx = SWIGLU ? 2L * K : (long)K;
+  u32x4 w[4], u[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = m0 + 4 * wave + r;
     w[r] = (u32x4){0u, 0u, 0u, 0u};
-    if (m < M && col_ok) w[r] = *reinterpret_cast<const u32x4*>(X + (long)m * K + col);
+    u[r] = (u32x4){0u, 0u, 0u, 0u};
+    if (m < M && col_ok) {
+      w[r] = *reinterpret_cast<const u32x4*>(X + (long)m * ldx + col);
+      if constexpr (SWIGLU) u[r] = *reinterpret_cast<const u32x4*>(X + (long)m * ldx + K + col);
+    }
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int rl = 4 * wave + r, m = m0 + rl;
     float v[8] = {bf16_lo(w[r].x), bf16_hi(w[r].x), bf16_lo(w[r].y), bf16_hi(w[r].y),
                   bf16_lo(w[r].z), bf16_hi(w[r].z), bf16_lo(w[r].w), bf16_hi(w[r].w)};
+    if constexpr (SWIGLU) {
+      const float up[8] = {bf16_lo(u[r].x), bf16_hi(u[r].x), bf16_lo(u[r].y), bf16_hi(u[r].y),
+                           bf16_lo(u[r].z), bf16_hi(u[r].z), bf16_lo(u[r].w), bf16_hi(u[r].w)};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = silu_fixed(v[i]) * up[i];
+    }
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -112,12 +177,13 @@ __global__ __launch_bounds__(kThreadsQ) void quant_rows_1x128(const uint16_t* __
 
 }  // namespace
 
-// Called by the public entry point in grouped_gemm.hip (which owns the error text).
-extern "C" __attribute__((visibility("hidden"))) mgg_status quantize_fp8_1x128_impl(
-    int M, int K, const void* X, void* Q, void* SF, mgg_sf_fmt sf, float sf_zero,
-    hipStream_t stream, const char** err) {
+namespace {
+
+mgg_status launch_quant(bool swiglu, int M, int K, const void* X, void* Q, void* SF,
+                        mgg_sf_fmt sf, float sf_zero, hipStream_t stream, const char** err) {
   if (M < 1 || K < 128 || K % 128 != 0) {
-    *err = "M must be positive and K a positive multiple of 128";
+    *err = swiglu ? "M must be positive and I a positive multiple of 128"
+                  : "M must be positive and K a positive multiple of 128";
     return MGG_EINVAL;
   }
   if (!X || !Q || !SF) {
@@ -125,7 +191,7 @@ extern "C" __attribute__((visibility("hidden"))) mgg_status quantize_fp8_1x128_i
     return MGG_EINVAL;
   }
   if ((uintptr_t)X % 16 || (uintptr_t)Q % 8 || (sf == MGG_SF_F32 && (uintptr_t)SF % 4)) {
-    *err = "X must be 16-byte, Q 8-byte and float32 scales 4-byte aligned";
+    *err = "the bf16 input must be 16-byte, Q 8-byte and float32 scales 4-byte aligned";
     return MGG_EINVAL;
   }
   if (sf != MGG_SF_F32 && sf != MGG_SF_UE8M0) {
@@ -136,22 +202,36 @@ extern "C" __attribute__((visibility("hidden"))) mgg_status quantize_fp8_1x128_i
     *err = "sf_zero must be a positive finite float";
     return MGG_EINVAL;
   }
-  if (K / 128 > 65535) {
-    *err = "K too large";
+  if (K / 128 > 65535 || (swiglu && K > INT_MAX / 2)) {
+    *err = swiglu ? "I too large" : "K too large";
     return MGG_EUNSUPPORTED;
   }
   const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock),
                   (unsigned)((K + kColsPerBlock - 1) / kColsPerBlock));
-  if (sf == MGG_SF_UE8M0)
-    hipLaunchKernelGGL(quant_rows_1x128<true>, grid, dim3(kThreadsQ), 0, stream,
-                       (const uint16_t*)X, (uint8_t*)Q, SF, M, K, sf_zero);
-  else
-    hipLaunchKernelGGL(quant_rows_1x128<false>, grid, dim3(kThreadsQ), 0, stream,
-                       (const uint16_t*)X, (uint8_t*)Q, SF, M, K, sf_zero);
+  const bool ue = sf == MGG_SF_UE8M0;
+  auto kern = swiglu ? (ue ? quant_rows_1x128<true, true> : quant_rows_1x128<false, true>)
+                     : (ue ? quant_rows_1x128<true, false> : quant_rows_1x128<false, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreadsQ), 0, stream, (const uint16_t*)X, (uint8_t*)Q,
+                     SF, M, K, sf_zero);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     *err = hipGetErrorString(e);
     return MGG_EHIP;
   }
   return MGG_OK;
+}
+
+}  // namespace
+
+// Called by the public entry points in grouped_gemm.hip (which own the error text).
+extern "C" __attribute__((visibility("hidden"))) mgg_status quantize_fp8_1x128_impl(
+    int M, int K, const void* X, void* Q, void* SF, mgg_sf_fmt sf, float sf_zero,
+    hipStream_t stream, const char** err) {
+  return launch_quant(false, M, K, X, Q, SF, sf, sf_zero, stream, err);
+}
+
+extern "C" __attribute__((visibility("hidden"))) mgg_status swiglu_quant_fp8_1x128_impl(
+    int M, int I, const void* H, void* Q, void* SF, mgg_sf_fmt sf, float sf_zero,
+    hipStream_t stream, const char** err) {
+  return launch_quant(true, M, I, H, Q, SF, sf, sf_zero, stream, err);
 }

@@ -37,9 +37,9 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for f in ("grouped_gemm_masked", "grouped_gemm_contiguous", "grouped_gemm_contiguous_psum",
               "grouped_gemm_kgrouped", "grouped_gemm_kgrouped_psum", "quantize_fp8_1x128",
-              "mgg_status_string", "mgg_last_error"):
+              "swiglu_quant_fp8_1x128", "mgg_status_string", "mgg_last_error"):
         assert f in names
-    assert len(names) == 8, names
+    assert len(names) == 9, names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -210,4 +210,29 @@ def quant(lib, M=64, K=256, X=P, Q=P, SF=P, sf=0, z=1.0):
 ])
 def test_quantize_rejects(lib, kw, code):
     assert quant(lib, **kw) == code
+    assert lib.mgg_last_error() != b""
+
+
+def swiglu_quant(lib, M=64, I=256, H=P, Q=P, SF=P, sf=0, z=1.0):
+    return lib.swiglu_quant_fp8_1x128(M, I, H, Q, SF, sf, ctypes.c_float(z), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=0), EINVAL),
+    (dict(M=-3), EINVAL),
+    (dict(I=0), EINVAL),
+    (dict(I=192), EINVAL),
+    (dict(H=NUL), EINVAL),
+    (dict(Q=NUL), EINVAL),
+    (dict(SF=NUL), EINVAL),
+    (dict(H=MIS), EINVAL),
+    (dict(Q=ctypes.c_void_p((1 << 20) + 4)), EINVAL),
+    (dict(SF=ctypes.c_void_p((1 << 20) + 2)), EINVAL),
+    (dict(sf=2), EINVAL),
+    (dict(z=0.0), EINVAL),
+    (dict(z=float("inf")), EINVAL),
+    (dict(I=128 * 65536), EUNSUPPORTED),
+])
+def test_swiglu_quantize_rejects(lib, kw, code):
+    assert swiglu_quant(lib, **kw) == code
     assert lib.mgg_last_error() != b""
