@@ -34,16 +34,28 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "moe_grouped_gemm_nt_amd", "csrc")
 
 
-def kernel_source_digest() -> str:
-    """SHA-256 over the kernel sources (names and bytes, sorted), so that HBM counter
-    readings taken on one version of the kernel are never reported for another."""
+KERNEL_NAME = "grouped_gemm_kernel"
+QUANT_KERNEL_NAME = "quant_rows_1x128"
+# the sources each kernel is compiled from (the public header only declares entry points)
+KERNEL_SOURCES = {
+    KERNEL_NAME: ("gemm_engine.h", "grouped_gemm_kernel.h", "grouped_gemm.hip"),
+    QUANT_KERNEL_NAME: ("quantize.hip",),
+}
+
+
+def kernel_name(workload: str) -> str:
+    return QUANT_KERNEL_NAME if workload in QUANT_WORKLOADS else KERNEL_NAME
+
+
+def kernel_source_digest(kernel: str = KERNEL_NAME) -> str:
+    """SHA-256 over the sources a kernel is built from (names and bytes), so that HBM
+    counter readings taken on one version of the kernel are never reported for another."""
     import hashlib
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".h", ".hip")):
-            h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+    for name in KERNEL_SOURCES[kernel]:
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
@@ -60,7 +72,7 @@ def measured_traffic(workload: str):
             m = re.match(r"^\s*-\s*([a-z_0-9-]+):\s*(\S+)", line)
             if m:
                 fields[m.group(1)] = m.group(2)
-    if fields.get("kernel-source-sha256") != kernel_source_digest():
+    if fields.get("kernel-source-sha256") != kernel_source_digest(kernel_name(workload)):
         return None
     try:
         return int(fields["fetch_bytes_per_launch"]) + int(fields["write_bytes_per_launch"])
@@ -143,6 +155,9 @@ def main():
         return
     if args.workload in QUANT_WORKLOADS:
         quant_bench(dev, args)
+        return
+    if args.workload == "contig_fp8_chain":
+        chain_bench(dev, args)
         return
     mgg.load_library()
     p, opt = synth.make_workload(args.workload, dev)
@@ -252,39 +267,27 @@ def main():
 
 
 QUANT_WORKLOADS = {
-    # bf16 activations -> FP8 E4M3 codes + 1x128 float32 scales: the expected tokens of the
+    # bf16 activations -> FP8 E4M3 codes + 1x128 scales: the expected tokens of the
     # 32-expert N=6144 configuration (32 x 192) at its hidden size 7168
-    "quant_fp8_1x128_6144x7168": (6144, 7168, "f32"),
-    "quant_fp8_1x128_ue8m0_6144x7168": (6144, 7168, "ue8m0"),
+    "quant_fp8_1x128_6144x7168": (6144, 7168, "f32", False),
+    "quant_fp8_1x128_ue8m0_6144x7168": (6144, 7168, "ue8m0", False),
+    # SwiGLU + re-quantization of the contiguous configuration's w13 output: 288 experts x
+    # 256-row budget = 73728 rows, 2I = 512 columns in, I = 256 out, UE8M0 scales
+    "swiglu_quant_fp8_ue8m0_73728x256": (73728, 256, "ue8m0", True),
+    # the same step for 4096 tokens at I = 2048
+    "swiglu_quant_fp8_4096x2048": (4096, 2048, "f32", True),
 }
 
 
-def quant_bench(dev, args):
-    """FP8 1x128 activation quantization: `steps` calls in one hipGraph, inputs rotated
-    over enough buffers to exceed the Infinity Cache; HBM roofline on the algorithmic
-    bytes (bf16 in, codes out, one scale per 128 elements)."""
+def _timed_graph(dev, stream, steps, fn):
+    """`steps` calls of fn(i) captured in one hipGraph and replayed once between events
+    recorded on the launch stream; returns ms per call."""
     import torch
-    import moe_grouped_gemm_nt_amd as mgg
-    mgg.load_library()
-    M, K, fmt = QUANT_WORKLOADS[args.workload]
-    sf_b = 4 if fmt == "f32" else 1
-    abytes = M * K * 2 + M * K + (K // 128) * M * sf_b
-    nrot = max(1, min(8, -(-2 * MALL_BYTES // (M * K * 3))))
-    g = torch.Generator(device=dev).manual_seed(0)
-    Xs = [torch.randn((M, K), device=dev, generator=g).to(torch.bfloat16) for _ in range(nrot)]
-    Qs = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(nrot)]
-    SFs = [torch.empty((K // 128, M), device=dev,
-                       dtype=torch.float32 if fmt == "f32" else torch.uint8) for _ in range(nrot)]
-    stream = torch.cuda.Stream(dev)
-    stream.wait_stream(torch.cuda.current_stream(dev))
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            mgg.quantize_fp8_1x128(Xs[i % nrot], Qs[i % nrot], SFs[i % nrot], fmt)
     torch.cuda.synchronize(dev)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
-        for i in range(args.steps):
-            mgg.quantize_fp8_1x128(Xs[i % nrot], Qs[i % nrot], SFs[i % nrot], fmt)
+        for i in range(steps):
+            fn(i)
     torch.cuda.synchronize(dev)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
@@ -292,7 +295,38 @@ def quant_bench(dev, args):
         graph.replay()
         t1.record(stream)
     torch.cuda.synchronize(dev)
-    ms_step = t0.elapsed_time(t1) / args.steps
+    return t0.elapsed_time(t1) / steps
+
+
+def quant_bench(dev, args):
+    """FP8 1x128 activation quantization (plain, or SwiGLU + quantization): `steps` calls
+    in one hipGraph, inputs rotated over enough buffers to exceed the Infinity Cache; HBM
+    roofline on the algorithmic bytes (bf16 in, codes out, one scale per 128 codes)."""
+    import torch
+    import moe_grouped_gemm_nt_amd as mgg
+    mgg.load_library()
+    M, K, fmt, swiglu = QUANT_WORKLOADS[args.workload]
+    sf_b = 4 if fmt == "f32" else 1
+    in_cols = 2 * K if swiglu else K
+    abytes = M * in_cols * 2 + M * K + (K // 128) * M * sf_b
+    nrot = max(1, min(8, -(-2 * MALL_BYTES // abytes)))
+    g = torch.Generator(device=dev).manual_seed(0)
+    Xs = [torch.randn((M, in_cols), device=dev, generator=g).to(torch.bfloat16)
+          for _ in range(nrot)]
+    Qs = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(nrot)]
+    SFs = [torch.empty((K // 128, M), device=dev,
+                       dtype=torch.float32 if fmt == "f32" else torch.uint8) for _ in range(nrot)]
+    fn = mgg.swiglu_quant_fp8_1x128 if swiglu else mgg.quantize_fp8_1x128
+
+    def step(i):
+        fn(Xs[i % nrot], Qs[i % nrot], SFs[i % nrot], fmt)
+
+    stream = torch.cuda.Stream(dev)
+    stream.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+    ms_step = _timed_graph(dev, stream, args.steps, step)
     gbs = abytes / (ms_step * 1e-3) / 1e9
     cpu = None
     if not args.no_cpu_baseline:
@@ -300,27 +334,101 @@ def quant_bench(dev, args):
         import oracle
         rows = 256
         x = Xs[0][:rows].cpu().view(torch.int16).numpy().view(np.uint16)
+        ofn = oracle.swiglu_quant_rows_1x128 if swiglu else oracle.quantize_rows_1x128
         passes, t = 0, 0.0
         w0 = time.perf_counter()
         while t < args.cpu_seconds and passes < 10000:
-            oracle.quantize_rows_1x128(x, fmt)
+            ofn(x, fmt)
             passes += 1
             t = time.perf_counter() - w0
-        cpu = {"value": round(rows * K * 3 * passes / t / 1e9, 4), "unit": "GB/s", "cores": 1,
-               "kind": "oracle", "sample": f"{rows} rows x {K} per pass; {passes} passes in {t:.1f} s"}
+        cpu = {"value": round(rows * abytes / M * passes / t / 1e9, 4), "unit": "GB/s",
+               "cores": 1, "kind": "oracle",
+               "sample": f"{rows} rows x {in_cols} per pass; {passes} passes in {t:.1f} s"}
+    what = "SwiGLU + FP8 1x128 re-quantization" if swiglu else "FP8 1x128 activation quantization"
     line = {
-        "metric": "FP8 1x128 activation quantization throughput (algorithmic bytes)",
+        "metric": f"{what} throughput (algorithmic bytes)",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16->e4m3", "data": "synthetic",
-        "config": {"workload": args.workload, "M": M, "K": K, "scales": fmt,
-                   "rotating_buffers": nrot, "timing": "one hipGraph of `steps` calls"},
+        "config": {"workload": args.workload, "M": M, ("I" if swiglu else "K"): K,
+                   "scales": fmt, "rotating_buffers": nrot,
+                   "timing": "one hipGraph of `steps` calls"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.workload),
                      "algorithmic_bytes_per_launch": abytes,
                      "avg_launch_us": round(ms_step * 1e3, 3)},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def chain_bench(dev, args):
+    """The expert chain of the contiguous configuration on one routing draw: FP8 tokens
+    [73728, 4096] -> w13 contiguous GEMM (288 experts, N = 512) -> SwiGLU + 1x128 UE8M0
+    re-quantization -> w2 contiguous GEMM (N = 4096, K = 256). Times the whole chain and
+    each of its three launches (each in its own hipGraph of `steps` calls)."""
+    import numpy as np
+    import torch
+    import moe_grouped_gemm_nt_amd as mgg
+    from moe_grouped_gemm_nt_amd import synth
+    mgg.load_library()
+    p, opt = synth.make_workload("contig_fp8_w13", dev)
+    em = opt["expected_m"]
+    I, Hd = p.N // 2, p.K
+    w2 = synth.make_contiguous("fp8", p.G, Hd, I, p.meta["seg_counts"], 3, dev, sf_fmt=p.sf_fmt,
+                               M_max=p.M)
+    B2, SFB2 = w2.B, w2.SFB
+    del w2
+    H = torch.empty((p.M, 2 * I), dtype=torch.bfloat16, device=dev)
+    Q = torch.empty((p.M, I), dtype=torch.uint8, device=dev)
+    SF = torch.empty((I // 128, p.M), dtype=torch.uint8, device=dev)
+    D = torch.empty((p.M, Hd), dtype=torch.bfloat16, device=dev)
+
+    def k13(i):
+        mgg.grouped_gemm_contiguous(p.A, p.B, H, p.m_indices, p.SFA, p.SFB, p.sfb_gran, em)
+
+    def kact(i):
+        mgg.swiglu_quant_fp8_1x128(H, Q, SF, sf_fmt=p.sf_fmt)
+
+    def k2(i):
+        mgg.grouped_gemm_contiguous(Q, B2, D, p.m_indices, SF, SFB2, p.sfb_gran, em)
+
+    def chain(i):
+        k13(i)
+        kact(i)
+        k2(i)
+
+    stream = torch.cuda.Stream(dev)
+    stream.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            chain(i)
+    ms = {name: _timed_graph(dev, stream, args.steps, fn)
+          for name, fn in (("chain", chain), ("w13", k13), ("swiglu_quant", kact), ("w2", k2))}
+    valid = int(p.meta["valid_rows"])
+    flops = {"w13": 2.0 * valid * p.N * p.K, "w2": 2.0 * valid * Hd * I}
+    total = flops["w13"] + flops["w2"]
+    tflops = total / (ms["chain"] * 1e-3) / 1e12
+    # dominant launch: the longer GEMM; MFMA roofline on its valid FLOPs
+    dom = max(("w13", "w2"), key=lambda k: ms[k])
+    dt = flops[dom] / (ms[dom] * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS["fp8"]
+    line = {
+        "metric": "MoE expert chain (w13 GEMM -> SwiGLU + FP8 quant -> w2 GEMM) TFLOPS "
+                  "(valid rows, both GEMMs)",
+        "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms["chain"], 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8", "data": "synthetic",
+        "config": {"workload": "contig_fp8_chain", "G": p.G, "M": p.M, "hidden": Hd,
+                   "intermediate": I, "valid_rows": valid, "expected_m": em,
+                   "scales": p.sf_fmt, "per_launch_us": {k: round(v * 1e3, 3)
+                                                         for k, v in ms.items()},
+                   "timing": "one hipGraph of `steps` calls per line"},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(dt, 1), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(dt / peak, 4), "traffic": None,
+                     "avg_launch_us": round(ms[dom] * 1e3, 3)},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 
@@ -347,7 +455,6 @@ def copy_calibration(dev, args):
           flush=True)
 
 
-KERNEL_NAME = "grouped_gemm_kernel"
 COPY_KERNEL_NAME = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 256 << 20
 
@@ -376,13 +483,14 @@ def summarize(args):
     out_dir = os.path.join(ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
     w = args.workload
+    kn = kernel_name(w)
     if args.summarize_trace:
         d = args.summarize_trace
-        stats = [r for r in _csv_rows(d, "kernel_stats.csv") if KERNEL_NAME in r["Name"]]
-        trace = [r for r in _csv_rows(d, "kernel_trace.csv") if KERNEL_NAME in r["Kernel_Name"]]
+        stats = [r for r in _csv_rows(d, "kernel_stats.csv") if kn in r["Name"]]
+        trace = [r for r in _csv_rows(d, "kernel_trace.csv") if kn in r["Kernel_Name"]]
         if not stats:
-            raise SystemExit(f"no {KERNEL_NAME} in {d}")
-        lines = [f"# {KERNEL_NAME}: kernel trace, workload {w}", "",
+            raise SystemExit(f"no {kn} in {d}")
+        lines = [f"# {kn}: kernel trace, workload {w}", "",
                  "Command (repository root, one MI355X):", "",
                  f"    rocprofv3 --kernel-trace --stats -d {d} -o {w} --output-format csv "
                  f"-- python -u bench.py --workload {w} --no-cpu-baseline", "",
@@ -400,7 +508,7 @@ def summarize(args):
                       f"lanes; VGPR {t.get('VGPR_Count')}, AGPR {t.get('Accum_VGPR_Count')}, "
                       f"SGPR {t.get('SGPR_Count')} (LDS is allocated dynamically, so the trace "
                       f"lists {t.get('LDS_Block_Size')} B of static LDS)."]
-        lines += ["", f"kernel-source-sha256 of the profiled build: {kernel_source_digest()}", ""]
+        lines += ["", f"kernel-source-sha256 of the profiled build: {kernel_source_digest(kn)}", ""]
         path = os.path.join(out_dir, f"{w}_kernel_trace.md")
         with open(path, "w") as f:
             f.write("\n".join(lines))
@@ -409,15 +517,15 @@ def summarize(args):
         cf, cw, kf, kw = args.summarize_traffic
         copy_f, _ = _counter_median(cf, COPY_KERNEL_NAME)
         copy_w, _ = _counter_median(cw, COPY_KERNEL_NAME)
-        ker_f, nf = _counter_median(kf, KERNEL_NAME)
-        ker_w, nw = _counter_median(kw, KERNEL_NAME)
+        ker_f, nf = _counter_median(kf, kn)
+        ker_w, nw = _counter_median(kw, kn)
         fac_f = COPY_BYTES / (copy_f * 1024.0)
         fac_w = COPY_BYTES / (copy_w * 1024.0)
         fetch = int(round(ker_f * 1024.0 * fac_f))
         write = int(round(ker_w * 1024.0 * fac_w))
         cmd = ("timeout -s KILL 120 rocprofv3 --pmc {c} -d {d} -o {o} --output-format csv -- "
                "python -u bench.py --workload {w} --steps {s} --warmup 2{x}")
-        lines = [f"# {KERNEL_NAME}: HBM traffic, workload {w}", "",
+        lines = [f"# {kn}: HBM traffic, workload {w}", "",
                  "Commands (repository root, one MI355X), one counter per run:", ""]
         for c, d, ww, o, s, x in [("FETCH_SIZE", cf, "copy_calibration", "copy", 10, ""),
                                   ("WRITE_SIZE", cw, "copy_calibration", "copy", 10, ""),
@@ -431,7 +539,7 @@ def summarize(args):
                   f"Kernel medians: FETCH_SIZE {ker_f:.1f} KiB over {nf} dispatches, "
                   f"WRITE_SIZE {ker_w:.1f} KiB over {nw} dispatches.", "",
                   "Values read by bench.py (bytes per launch, after scaling):", "",
-                  f"- kernel-source-sha256: {kernel_source_digest()}",
+                  f"- kernel-source-sha256: {kernel_source_digest(kn)}",
                   f"- fetch_bytes_per_launch: {fetch}",
                   f"- write_bytes_per_launch: {write}", ""]
         path = os.path.join(out_dir, f"{w}_hbm_traffic.md")

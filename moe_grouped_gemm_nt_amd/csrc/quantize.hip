@@ -19,8 +19,8 @@
 // SF [K/128][M] (float32 or one byte per scale) — the activation-scale layout the GEMM
 // entry points read.
 //
-// One workgroup handles 16 rows x 512 columns (see quant_rows_1x128); the group maximum
-// is a 16-lane butterfly. The kernel is HBM-bound (3 bytes per element; 5 for SwiGLU).
+// One workgroup handles 64 (row, 128-column group) units (see quant_rows_1x128); the
+// group maximum is a 16-lane butterfly. The kernel is HBM-bound (3 bytes per element; 5 for SwiGLU).
 
 #include <hip/hip_runtime.h>
 #include <limits.h>
@@ -30,8 +30,7 @@
 
 namespace {
 
-constexpr int kRowsPerBlock = 16;  // 4 waves x 4 rows
-constexpr int kColsPerBlock = 512;  // one wave instruction covers 512 contiguous columns
+constexpr int kUnitsPerBlock = 64;  // (row, 128-column group) units: 16 quarters x 4 steps
 constexpr int kThreadsQ = 256;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -98,38 +97,46 @@ __device__ __forceinline__ float silu_fixed(float x) {
   return x / d;
 }
 
-// One workgroup: 16 rows x 512 columns. Wave w takes rows 4w .. 4w + 3 of the block; in
-// each, lanes 16 g .. 16 g + 15 cover 128-column group g (8 elements per lane), so one
-// load instruction reads 1 KB of a row contiguously. The 64 scales of the block are
-// collected in LDS and written as four runs of 16 consecutive rows. With SWIGLU, X has
-// 2K columns per row and each lane also loads the matching up-projection columns K + col.
+// One workgroup covers 64 (row, 128-column group) units: GB = 2^gb_log groups side by
+// side (GB = 4 for rows of at least 512 columns, fewer for narrower rows so no lane idles)
+// times 64 / GB rows. Each 16-lane quarter of a wave takes one unit per step (8 elements
+// per lane, one contiguous 256-byte run of the row), the quarters of a wave cover GB
+// adjacent groups of 4 / GB consecutive rows, and each wave does four steps. The 64 scales
+// of the block are collected in LDS and written as GB runs of consecutive rows. With
+// SWIGLU, X has 2K columns per row and each lane also loads the matching up-projection
+// columns K + col.
 template <bool UE8M0, bool SWIGLU>
 __global__ __launch_bounds__(kThreadsQ) void quant_rows_1x128(const uint16_t* __restrict__ X,
                                                               uint8_t* __restrict__ Q,
                                                               void* __restrict__ SF, int M,
-                                                              int K, float sf_zero) {
-  __shared__ uint32_t s_sf[4][kRowsPerBlock];  // [group][row] scale bits or codes
+                                                              int K, float sf_zero,
+                                                              int gb_log) {
+  __shared__ uint32_t s_sf[kUnitsPerBlock];  // [group][row] scale bits or codes
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane >> 4, l16 = lane & 15;
-  const int m0 = blockIdx.x * kRowsPerBlock;
-  const int kb = blockIdx.y * 4 + grp;  // this lane's 128-column group
-  const bool col_ok = kb * 128 < K;     // uniform per 16-lane group
-  const long col = (long)kb * 128 + l16 * 8;
+  const int rows_log = 6 - gb_log;  // 64 / GB rows per block
+  const int m0 = blockIdx.x << rows_log;
   const long ldx = SWIGLU ? 2L * K : (long)K;
   u32x4 w[4], u[4];
+  int rl[4], kb[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int m = m0 + 4 * wave + r;
+    const int unit = (wave * 4 + r) * 4 + grp;
+    rl[r] = unit >> gb_log;
+    kb[r] = (blockIdx.y << gb_log) + (unit & ((1 << gb_log) - 1));
+    const int m = m0 + rl[r];
+    const long col = (long)kb[r] * 128 + l16 * 8;
     w[r] = (u32x4){0u, 0u, 0u, 0u};
     u[r] = (u32x4){0u, 0u, 0u, 0u};
-    if (m < M && col_ok) {
+    if (m < M && kb[r] * 128 < K) {  // uniform per 16-lane quarter
       w[r] = *reinterpret_cast<const u32x4*>(X + (long)m * ldx + col);
       if constexpr (SWIGLU) u[r] = *reinterpret_cast<const u32x4*>(X + (long)m * ldx + K + col);
     }
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int rl = 4 * wave + r, m = m0 + rl;
+    const int m = m0 + rl[r];
+    const long col = (long)kb[r] * 128 + l16 * 8;
     float v[8] = {bf16_lo(w[r].x), bf16_hi(w[r].x), bf16_lo(w[r].y), bf16_hi(w[r].y),
                   bf16_lo(w[r].z), bf16_hi(w[r].z), bf16_lo(w[r].w), bf16_hi(w[r].w)};
     if constexpr (SWIGLU) {
@@ -159,18 +166,19 @@ __global__ __launch_bounds__(kThreadsQ) void quant_rows_1x128(const uint16_t* __
     u32x2 out;
     out.x = to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
     out.y = to_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
-    if (m < M && col_ok) *reinterpret_cast<u32x2*>(Q + (long)m * K + col) = out;
-    if (l16 == 0) s_sf[grp][rl] = sfbits;
+    if (m < M && kb[r] * 128 < K) *reinterpret_cast<u32x2*>(Q + (long)m * K + col) = out;
+    const int g = kb[r] - (blockIdx.y << gb_log);
+    if (l16 == 0) s_sf[(g << rows_log) + rl[r]] = sfbits;
   }
   __syncthreads();
-  if (threadIdx.x < 4 * kRowsPerBlock) {
-    const int g = threadIdx.x / kRowsPerBlock, rl = threadIdx.x % kRowsPerBlock;
-    const int m = m0 + rl, k2 = blockIdx.y * 4 + g;
+  if (threadIdx.x < kUnitsPerBlock) {
+    const int g = threadIdx.x >> rows_log, r = threadIdx.x & ((1 << rows_log) - 1);
+    const int m = m0 + r, k2 = (blockIdx.y << gb_log) + g;
     if (m < M && k2 * 128 < K) {
       if constexpr (UE8M0)
-        reinterpret_cast<uint8_t*>(SF)[(long)k2 * M + m] = (uint8_t)s_sf[g][rl];
+        reinterpret_cast<uint8_t*>(SF)[(long)k2 * M + m] = (uint8_t)s_sf[threadIdx.x];
       else
-        reinterpret_cast<uint32_t*>(SF)[(long)k2 * M + m] = s_sf[g][rl];
+        reinterpret_cast<uint32_t*>(SF)[(long)k2 * M + m] = s_sf[threadIdx.x];
     }
   }
 }
@@ -206,13 +214,16 @@ mgg_status launch_quant(bool swiglu, int M, int K, const void* X, void* Q, void*
     *err = swiglu ? "I too large" : "K too large";
     return MGG_EUNSUPPORTED;
   }
-  const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock),
-                  (unsigned)((K + kColsPerBlock - 1) / kColsPerBlock));
+  const int kgroups = K / 128;
+  const int gb_log = kgroups >= 4 ? 2 : kgroups >= 2 ? 1 : 0;
+  const int rows = kUnitsPerBlock >> gb_log;
+  const dim3 grid((unsigned)((M + rows - 1) / rows),
+                  (unsigned)((kgroups + (1 << gb_log) - 1) >> gb_log));
   const bool ue = sf == MGG_SF_UE8M0;
   auto kern = swiglu ? (ue ? quant_rows_1x128<true, true> : quant_rows_1x128<false, true>)
                      : (ue ? quant_rows_1x128<true, false> : quant_rows_1x128<false, false>);
   hipLaunchKernelGGL(kern, grid, dim3(kThreadsQ), 0, stream, (const uint16_t*)X, (uint8_t*)Q,
-                     SF, M, K, sf_zero);
+                     SF, M, K, sf_zero, gb_log);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     *err = hipGetErrorString(e);
