@@ -21,15 +21,21 @@ Parity status of each function (what pins it lives in tests/test_oracle_*.py):
   exp_f32, silu_f32, swiglu_values, swiglu_quant_rows_1x128   pinned (float64 exp and
       torch's silu within a few ulps, special values, exact cases where silu(x) = x,
       equality with the plain quantization of exactly representable products)
+  decode_e2m1, unpack_fp4, the "fp8_fp4" dtype of the M-grouped products   pinned
+      (the format's value table, literal nibble cases, exact-rational brute force over
+      raw bytes, one-hot weights, equality with the FP8 channel-scale product when the
+      four block scales of each 128-K group agree)
 """
 
 from .formats import (  # noqa: F401
     E4M3_MAX,
     decode_bf16,
+    decode_e2m1,
     decode_e4m3fn,
     decode_scale,
     decode_ue8m0,
     round_to_bf16,
+    unpack_fp4,
 )
 from .quantize import (  # noqa: F401
     encode_e4m3_rne,
@@ -44,6 +50,7 @@ from .swiglu import (  # noqa: F401
     swiglu_values,
 )
 from .grouped_gemm import (  # noqa: F401
+    MX_BLOCK,
     SCALE_K,
     calc_diff,
     contiguous_row_expert,

@@ -14,6 +14,11 @@ float64 values, so products of a decoded FP8 code and an fp32 scale are exact to
 * UE8M0: an unsigned 8-bit biased exponent, value 2^(u-127), code 255 is NaN (the
   power-of-two "2^k" scales named in the environment section of the DeepGEMM issue
   "SM120 m_grouped_fp8 contiguous kernel: illegal memory access at CUDA graph replay").
+* E2M1 (FP4, the element type of the "fp8_fp4" kernel family that issue names, from the
+  OCP microscaling formats): 1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit, no
+  infinities or NaN; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. Two codes per byte; the
+  pages do not state the packing, and the reading taken is the even element in the low
+  nibble.
 """
 
 from __future__ import annotations
@@ -46,6 +51,41 @@ def decode_e4m3fn(codes) -> np.ndarray:
     if codes.dtype != np.uint8:
         raise TypeError(f"E4M3 codes must be uint8, got {codes.dtype}")
     return _E4M3_TABLE[codes]
+
+
+def _e2m1_value(code: int) -> float:
+    """Exact value of one E2M1 code (0..15), from the field definitions."""
+    sign = -1.0 if (code >> 3) & 1 else 1.0
+    exp = (code >> 1) & 0x3
+    man = code & 0x1
+    if exp == 0:  # subnormal: 0.m * 2^(1-1)
+        return sign * (man / 2.0)
+    return sign * (1.0 + man / 2.0) * 2.0 ** (exp - 1)
+
+
+_E2M1_TABLE = np.array([_e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def decode_e2m1(codes) -> np.ndarray:
+    """E2M1 codes 0..15 (uint8, any shape) -> float64 values."""
+    codes = np.asarray(codes)
+    if codes.dtype != np.uint8:
+        raise TypeError(f"E2M1 codes must be uint8, got {codes.dtype}")
+    if (codes > 15).any():
+        raise ValueError("E2M1 codes are 4-bit")
+    return _E2M1_TABLE[codes]
+
+
+def unpack_fp4(packed) -> np.ndarray:
+    """Packed FP4 bytes [..., K/2] -> codes [..., K]: element 2i is the low nibble of
+    byte i, element 2i + 1 the high nibble."""
+    packed = np.asarray(packed)
+    if packed.dtype != np.uint8:
+        raise TypeError(f"packed FP4 must be uint8, got {packed.dtype}")
+    out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), np.uint8)
+    out[..., 0::2] = packed & 0x0F
+    out[..., 1::2] = packed >> 4
+    return out
 
 
 def decode_bf16(bits) -> np.ndarray:

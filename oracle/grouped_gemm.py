@@ -27,6 +27,13 @@ What is computed, and where it is defined:
   per 128 global tokens; D_e = C_e + A_e^T-style product over the expert's tokens, with
   C aliasing D (the script passes the zeroed output as both `d` and `c`).
 
+* FP8 x FP4 ("fp8_fp4", the kernel family of the SM120 issue, named there but not
+  described): activations are FP8 E4M3 with their 1x128 scales as above; weights are
+  FP4 E2M1, two per byte, with one UE8M0 scale per 32 consecutive K of a weight row (the
+  OCP microscaling block), stored per expert as [K/128][N][4] (byte j of a [kb][n] entry
+  scales K elements 128 kb + 32 j .. + 31 of row n). The weight-scale granularity is
+  called "block32".
+
 FP8 dequantization: value = decode(code) * scale, exact in float64. The GEMM itself is
 the plain definition sum_k Ahat[m, k] * Bhat[n, k], evaluated by numpy's float64 matmul
 (a library primitive, no reordering beyond its own). Outputs stay float64; rounding to
@@ -41,9 +48,10 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import decode_bf16, decode_e4m3fn, decode_scale
+from .formats import decode_bf16, decode_e2m1, decode_e4m3fn, decode_scale, decode_ue8m0, unpack_fp4
 
 SCALE_K = 128  # K elements sharing one scale (recipe (1, 1, 128) of the K-grouped call)
+MX_BLOCK = 32  # K elements sharing one FP4 weight scale
 
 
 # --------------------------------------------------------------------------- helpers
@@ -52,7 +60,7 @@ SCALE_K = 128  # K elements sharing one scale (recipe (1, 1, 128) of the K-group
 def _decode_elems(dtype: str, codes) -> np.ndarray:
     if dtype == "bf16":
         return decode_bf16(codes)
-    if dtype == "fp8":
+    if dtype in ("fp8", "fp8_fp4"):  # activations of the FP8 x FP4 product are FP8
         return decode_e4m3fn(codes)
     raise ValueError(f"unknown dtype {dtype!r}")
 
@@ -82,7 +90,17 @@ def dequant_weight_rows(dtype, codes_rows, n_index, sfb=None, sfb_gran="block128
     `codes_rows` holds the codes of those rows. FP8 scales of one expert:
       block128: sfb[ceil(N/128), K/128], one scale per 128x128 block;
       channel:  sfb[K/128, N], one scale per row n and 128-K group.
+    FP4 ("fp8_fp4"): `codes_rows` are packed bytes [R, K/2]; scales (always UE8M0)
+      block32:  sfb[K/128, N, 4], one scale per row n and 32-K block.
     """
+    if dtype == "fp8_fp4":
+        if sfb_gran != "block32":
+            raise ValueError("FP4 weights take block32 scales")
+        vals = decode_e2m1(unpack_fp4(codes_rows))
+        n_index = np.asarray(n_index)
+        sf = decode_ue8m0(np.asarray(sfb))  # [K/128, N, 4]
+        per_row = sf[:, n_index, :].transpose(1, 0, 2).reshape(n_index.size, -1)  # [R, K/32]
+        return vals * np.repeat(per_row, MX_BLOCK, axis=1)[:, :vals.shape[1]]
     vals = _decode_elems(dtype, codes_rows)
     if dtype == "bf16":
         return vals
