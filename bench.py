@@ -28,7 +28,9 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}
+# dense MFMA peaks; an FP8 x FP4 product is priced at the FP8 rate (the faster FP4 rate
+# needs FP4 on both operands)
+MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "fp8_fp4": 5033.2}
 MALL_BYTES = 256 << 20
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "moe_grouped_gemm_nt_amd", "csrc")
@@ -107,7 +109,8 @@ def algorithmic_bytes(p, opt) -> int:
     output once, every scale once, valid output rows written once (read once more when
     accumulating)."""
     import numpy as np
-    esz = 1 if p.dtype == "fp8" else 2
+    esz = 2 if p.dtype == "bf16" else 1
+    wsz = 0.5 if p.dtype == "fp8_fp4" else esz  # weight bytes per element
     sf = 4 if p.sf_fmt == "f32" else 1
     if p.variant == "kgrouped":
         T = int(np.sum(p.meta["ks"]))
@@ -123,11 +126,13 @@ def algorithmic_bytes(p, opt) -> int:
         idx = p.meta["m_indices"]
         rows = int((idx >= 0).sum())
         experts = len(set(idx[idx >= 0].tolist()))
-    b = rows * p.K * esz + experts * p.N * p.K * esz + rows * p.N * 2
-    if p.dtype == "fp8":
+    b = rows * p.K * esz + int(experts * p.N * p.K * wsz) + rows * p.N * 2
+    if p.dtype != "bf16":
         kb = p.K // 128
         b += rows * kb * sf
-        b += experts * (((p.N + 127) // 128) * kb if p.sfb_gran == "block128" else p.N * kb) * sf
+        wscales = {"block128": ((p.N + 127) // 128) * kb, "channel": p.N * kb,
+                   "block32": p.N * kb * 4}[p.sfb_gran]
+        b += experts * wscales * sf
     return b
 
 

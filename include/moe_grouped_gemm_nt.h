@@ -38,6 +38,16 @@
  *    either float32 (MGG_SF_F32) or one unsigned byte u per scale meaning 2^(u-127)
  *    (MGG_SF_UE8M0). A scale covers 128 consecutive K elements of one row (1x128) or
  *    a 128x128 block of a weight matrix.
+ *  - FP8 x FP4 (MGG_FP8_FP4, the "fp8_fp4" kernel family the DeepGEMM issue "SM120
+ *    m_grouped_fp8 contiguous kernel: illegal memory access at CUDA graph replay" names
+ *    without describing it; the format reading is this library's): activations are FP8
+ *    E4M3 with 1x128 UE8M0 scales; weights are FP4 E2M1 (OCP microscaling: 1 sign, 2
+ *    exponent, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte with
+ *    the even K element in the low nibble, so a weight row is K/2 bytes; each weight row
+ *    has one UE8M0 scale per 32 consecutive K (MGG_SFB_BLOCK32), stored per expert as
+ *    [K/128][N][4] bytes (byte j of entry [kb][n] scales K 128 kb + 32 j .. + 31). Only
+ *    the M-grouped entry points take it (the K-grouped ones return MGG_EUNSUPPORTED),
+ *    and only with MGG_SF_UE8M0 (else MGG_EUNSUPPORTED).
  *  - Accumulation is FP32; BF16 outputs are rounded to nearest even.
  *  - Inputs must not overlap outputs (except C == D in grouped_gemm_kgrouped).
  *  - Calls on one stream are ordered; calls that run concurrently on different streams
@@ -60,25 +70,31 @@ typedef enum {
   MGG_EHIP = 3          /* the HIP runtime reported an error at launch */
 } mgg_status;
 
-typedef enum { MGG_BF16 = 0, MGG_FP8_E4M3 = 1 } mgg_dtype;
+typedef enum {
+  MGG_BF16 = 0,      /* both operands bfloat16 */
+  MGG_FP8_E4M3 = 1,  /* both operands FP8 E4M3 */
+  MGG_FP8_FP4 = 2    /* FP8 E4M3 activations, FP4 E2M1 weights (M-grouped entry points) */
+} mgg_dtype;
 typedef enum { MGG_SF_F32 = 0, MGG_SF_UE8M0 = 1 } mgg_sf_fmt;
 typedef enum {
   MGG_SFB_BLOCK128 = 0, /* one weight scale per 128x128 block */
-  MGG_SFB_CHANNEL = 1   /* one weight scale per weight row and 128-K group */
+  MGG_SFB_CHANNEL = 1,  /* one weight scale per weight row and 128-K group */
+  MGG_SFB_BLOCK32 = 2   /* FP4 weights: one UE8M0 scale per weight row and 32-K block */
 } mgg_sfb_gran;
 
 /*
  * Masked M-grouped NT GEMM: for every expert g and valid row m < clamp(masked_m[g], 0,
  * cap), D[g, m, n] = sum_k A[g, m, k] * B[g, n, k] (dequantized for FP8).
  *
- *   dt          MGG_BF16 or MGG_FP8_E4M3 (both operands).
+ *   dt          MGG_BF16, MGG_FP8_E4M3 (both operands) or MGG_FP8_FP4.
  *   G, cap      experts and rows per expert (capacity); 1 <= G <= 4096, cap >= 1.
  *   N, K        N >= 1 with N % 8 == 0; K >= 1 with K % 8 == 0 (BF16), K % 128 == 0 (FP8).
  *   A           [G][cap][K] elements (bf16 or e4m3 bytes); 16-byte aligned.
  *   SFA         FP8 only (else NULL): activation scales [G][K/128][cap], one per row and
  *               128-K group, rows contiguous within each group.
- *   B           [G][N][K] elements; 16-byte aligned.
- *   SFB         FP8 only: BLOCK128 -> [G][ceil(N/128)][K/128]; CHANNEL -> [G][K/128][N].
+ *   B           [G][N][K] elements (FP4: [G][N][K/2] bytes); 16-byte aligned.
+ *   SFB         FP8 only: BLOCK128 -> [G][ceil(N/128)][K/128]; CHANNEL -> [G][K/128][N];
+ *               BLOCK32 (FP4 weights) -> [G][K/128][N][4].
  *   sf, gran    scale storage format and weight-scale granularity (ignored for BF16).
  *   D           bf16 [G][cap][N]; 16-byte aligned. Only valid rows are written: padding
  *               rows and every byte outside the valid rows keep their previous contents.

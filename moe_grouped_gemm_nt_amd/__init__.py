@@ -7,11 +7,11 @@ kernels of libmoe_grouped_gemm_nt.so; there is no fallback of any kind, and call
 entry point without the built library raises.
 
 Entry points (same names as the C functions):
-    grouped_gemm_masked(A, B, D, masked_m, SFA=None, SFB=None, sfb_gran="block128",
+    grouped_gemm_masked(A, B, D, masked_m, SFA=None, SFB=None, sfb_gran=None,
                         expected_m=0)
-    grouped_gemm_contiguous(A, B, D, m_indices, SFA=None, SFB=None, sfb_gran="block128",
+    grouped_gemm_contiguous(A, B, D, m_indices, SFA=None, SFB=None, sfb_gran=None,
                             expected_m=0)
-    grouped_gemm_contiguous_psum(A, B, D, psum, SFA=None, SFB=None, sfb_gran="block128",
+    grouped_gemm_contiguous_psum(A, B, D, psum, SFA=None, SFB=None, sfb_gran=None,
                                  expected_m=0)
     grouped_gemm_kgrouped(A, B, D, ks, M, N, SFA=None, SFB=None, accumulate=True,
                           psum=False)   (psum=True calls grouped_gemm_kgrouped_psum)
@@ -19,7 +19,10 @@ Entry points (same names as the C functions):
     swiglu_quant_fp8_1x128(H, Q=None, SF=None, sf_fmt="f32", sf_zero=1.0) -> (Q, SF)
 
 Element types: bfloat16 tensors select BF16; uint8 (or float8_e4m3fn) tensors select
-FP8 E4M3. Scale tensors: float32 selects FP32 scales, uint8 selects UE8M0 scales.
+FP8 E4M3; FP8 activations with weights of K/2 bytes per row (uint8 or float4_e2m1fn_x2)
+select FP8 x FP4 (E2M1 weights, two per byte, 1x32 UE8M0 weight scales "block32").
+Scale tensors: float32 selects FP32 scales, uint8 selects UE8M0 scales. `sfb_gran`
+defaults to "block128" (FP8) or "block32" (FP4 weights).
 """
 
 from __future__ import annotations
@@ -43,10 +46,10 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libmoe_grouped_gemm_nt.so"
 _lib = None
 
-MGG_BF16, MGG_FP8_E4M3 = 0, 1
+MGG_BF16, MGG_FP8_E4M3, MGG_FP8_FP4 = 0, 1, 2
 MGG_SF_F32, MGG_SF_UE8M0 = 0, 1
-MGG_SFB_BLOCK128, MGG_SFB_CHANNEL = 0, 1
-_GRAN = {"block128": MGG_SFB_BLOCK128, "channel": MGG_SFB_CHANNEL}
+MGG_SFB_BLOCK128, MGG_SFB_CHANNEL, MGG_SFB_BLOCK32 = 0, 1, 2
+_GRAN = {"block128": MGG_SFB_BLOCK128, "channel": MGG_SFB_CHANNEL, "block32": MGG_SFB_BLOCK32}
 
 
 class MggError(RuntimeError):
@@ -118,6 +121,21 @@ def _elem_dtype(t) -> int:
     raise TypeError(f"operands must be bfloat16 or FP8 bytes, got {t.dtype}")
 
 
+def _m_operands(A, B, K):
+    """Element type of an M-grouped call from the operand tensors: bf16 x bf16, FP8 x
+    FP8 (B [G, N, K] bytes) or FP8 x FP4 (B [G, N, K/2] packed bytes, or torch's packed
+    float4 type); returns (dtype code, default weight-scale granularity)."""
+    import torch
+    dt = _elem_dtype(A)
+    fp4_t = getattr(torch, "float4_e2m1fn_x2", None)
+    if dt == MGG_FP8_E4M3 and B.dim() == 3 and 2 * B.shape[2] == K and \
+            B.dtype in (torch.uint8, fp4_t):
+        return MGG_FP8_FP4, "block32"
+    _require(B.dim() == 3 and B.shape[2] == K, "B must be [G, N, K] (FP4 weights: [G, N, K/2])")
+    _require(_elem_dtype(B) == dt, "A and B must have the same element type")
+    return dt, "block128"
+
+
 def _sf_fmt(sf) -> int:
     import torch
     if sf is None:
@@ -146,7 +164,7 @@ def _contig(*ts):
             _require(t.is_contiguous(), "tensors must be contiguous")
 
 
-def grouped_gemm_masked(A, B, D, masked_m, SFA=None, SFB=None, sfb_gran="block128",
+def grouped_gemm_masked(A, B, D, masked_m, SFA=None, SFB=None, sfb_gran=None,
                         expected_m=0):
     """D[g, m, :] = A[g, m, :] @ B[g].T for m < masked_m[g]; A[G, cap, K], B[G, N, K],
     D bf16 [G, cap, N], masked_m int32 [G] on the device."""
@@ -156,11 +174,11 @@ def grouped_gemm_masked(A, B, D, masked_m, SFA=None, SFB=None, sfb_gran="block12
     _contig(A, B, D, masked_m, SFA, SFB)
     G, cap, K = A.shape
     N = B.shape[1]
-    _require(tuple(B.shape) == (G, N, K), "B must be [G, N, K]")
+    dt, gran = _m_operands(A, B, K)
+    _require(B.shape[0] == G, "B must hold G experts")
     _require(tuple(D.shape) == (G, cap, N) and D.dtype == torch.bfloat16, "D must be bf16 [G, cap, N]")
     _require(masked_m.dtype == torch.int32 and masked_m.numel() == G, "masked_m must be int32 [G]")
-    dt = _elem_dtype(A)
-    _require(_elem_dtype(B) == dt, "A and B must have the same element type")
+    sfb_gran = sfb_gran or gran
     with torch.cuda.device(A.device):
         _check(lib.grouped_gemm_masked(dt, G, cap, N, K, _ptr(A), _ptr(SFA), _ptr(B), _ptr(SFB),
                                        _sf_fmt(SFA), _GRAN[sfb_gran], _ptr(D), _ptr(masked_m),
@@ -168,7 +186,7 @@ def grouped_gemm_masked(A, B, D, masked_m, SFA=None, SFB=None, sfb_gran="block12
     return D
 
 
-def grouped_gemm_contiguous(A, B, D, m_indices, SFA=None, SFB=None, sfb_gran="block128",
+def grouped_gemm_contiguous(A, B, D, m_indices, SFA=None, SFB=None, sfb_gran=None,
                             expected_m=0):
     """D[r, :] = A[r, :] @ B[m_indices[r]].T for rows with a valid expert index;
     A[M, K], B[G, N, K], D bf16 [M, N], m_indices int32 [M] on the device."""
@@ -178,11 +196,10 @@ def grouped_gemm_contiguous(A, B, D, m_indices, SFA=None, SFB=None, sfb_gran="bl
     _contig(A, B, D, m_indices, SFA, SFB)
     M, K = A.shape
     G, N, _ = B.shape
-    _require(B.shape[2] == K, "B must be [G, N, K]")
+    dt, gran = _m_operands(A, B, K)
     _require(tuple(D.shape) == (M, N) and D.dtype == torch.bfloat16, "D must be bf16 [M, N]")
     _require(m_indices.dtype == torch.int32 and m_indices.numel() == M, "m_indices must be int32 [M]")
-    dt = _elem_dtype(A)
-    _require(_elem_dtype(B) == dt, "A and B must have the same element type")
+    sfb_gran = sfb_gran or gran
     with torch.cuda.device(A.device):
         _check(lib.grouped_gemm_contiguous(dt, G, M, N, K, _ptr(A), _ptr(SFA), _ptr(B), _ptr(SFB),
                                            _sf_fmt(SFA), _GRAN[sfb_gran], _ptr(D),
@@ -190,7 +207,7 @@ def grouped_gemm_contiguous(A, B, D, m_indices, SFA=None, SFB=None, sfb_gran="bl
     return D
 
 
-def grouped_gemm_contiguous_psum(A, B, D, psum, SFA=None, SFB=None, sfb_gran="block128",
+def grouped_gemm_contiguous_psum(A, B, D, psum, SFA=None, SFB=None, sfb_gran=None,
                                  expected_m=0):
     """D[r, :] = A[r, :] @ B[e].T for r in expert e's row segment [psum[e-1], psum[e])
     (ends clamped to [0, M] and made non-decreasing); A[M, K], B[G, N, K], D bf16 [M, N],
@@ -201,11 +218,10 @@ def grouped_gemm_contiguous_psum(A, B, D, psum, SFA=None, SFB=None, sfb_gran="bl
     _contig(A, B, D, psum, SFA, SFB)
     M, K = A.shape
     G, N, _ = B.shape
-    _require(B.shape[2] == K, "B must be [G, N, K]")
+    dt, gran = _m_operands(A, B, K)
     _require(tuple(D.shape) == (M, N) and D.dtype == torch.bfloat16, "D must be bf16 [M, N]")
     _require(psum.dtype == torch.int32 and psum.numel() == G, "psum must be int32 [G]")
-    dt = _elem_dtype(A)
-    _require(_elem_dtype(B) == dt, "A and B must have the same element type")
+    sfb_gran = sfb_gran or gran
     with torch.cuda.device(A.device):
         _check(lib.grouped_gemm_contiguous_psum(dt, G, M, N, K, _ptr(A), _ptr(SFA), _ptr(B),
                                                 _ptr(SFB), _sf_fmt(SFA), _GRAN[sfb_gran],

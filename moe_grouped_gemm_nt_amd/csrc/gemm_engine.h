@@ -25,9 +25,11 @@
 // weight rows of a wave are further permuted so that one lane holds 4*NI consecutive
 // n, which turns the epilogue into full 16-byte row-contiguous stores.
 //
-// K order. Inside one MFMA the K elements a lane supplies may be any fixed permutation
-// as long as both operands use the same one; lanes 16g..16g+15 supply the 16-byte K
-// chunks g and g+4 of each 128-byte slice (FP8). Across slices K ascends. The layout,
+// K order. The 16x16x128 FP8 operand of lanes 16g..16g+15 holds K 16g..16g+15 in its
+// first four registers and K 64+16g..64+16g+15 in the last four, so those lanes read
+// the 16-byte chunks g and g+4 of each 128-byte slice; an FP4 operand's lanes
+// 16g..16g+15 hold K 32g..32g+31 (the 16-byte chunk g of a 64-byte FP4 slice), and the
+// MX scale a lane passes covers exactly those 32 elements. Across slices K ascends. The layout,
 // the instruction and the promotion formula do not depend on the tile shape, so every
 // tile configuration produces the same bits.
 #pragma once
@@ -44,9 +46,11 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 enum Variant { kMasked = 0, kContig = 1, kKGrouped = 2, kPsum = 3 };
-enum DType { kBF16 = 0, kFP8 = 1 };
+// kFP4W: FP8 E4M3 activations times FP4 E2M1 weights (two per byte, even K element in
+// the low nibble) with one UE8M0 scale per 32 K of a weight row.
+enum DType { kBF16 = 0, kFP8 = 1, kFP4W = 2 };
 enum SfFmt { kSfF32 = 0, kSfUE8M0 = 1 };
-enum SfbGran { kSfbBlock = 0, kSfbChannel = 1 };
+enum SfbGran { kSfbBlock = 0, kSfbChannel = 1, kSfbBlock32 = 2 };
 
 constexpr int kThreads = 256;     // one group of four waves
 // Tiles of accumulation input in flight per epilogue wave. Deeper prefetch measured

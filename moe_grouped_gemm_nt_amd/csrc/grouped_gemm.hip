@@ -139,7 +139,7 @@ mgg_status launch_tile(TileId tile, const Params& p, hipStream_t s) {
   // The largest tile needs the most LDS; fall back to the middle one when the
   // scheduler table does not fit next to it.
   if (tile == kTileL && lds_bytes<TileL, VAR, DT, SF, GRAN, false>(p) > kLdsBytes) tile = kTileM;
-  using TileS = std::conditional_t<DT == kFP8, TileS8, TileS16>;
+  using TileS = std::conditional_t<DT == kBF16, TileS16, TileS8>;
   switch (tile) {
     case kTileS: return launch<TileS, VAR, DT, SF, GRAN, false>(p, m_tiles<TileS, VAR>(p), s);
     case kTileM: return launch<TileM, VAR, DT, SF, GRAN, false>(p, m_tiles<TileM, VAR>(p), s);
@@ -152,6 +152,7 @@ template <int VAR>
 mgg_status dispatch_m(mgg_dtype dt, mgg_sf_fmt sf, mgg_sfb_gran gran, TileId tile,
                       const Params& p, hipStream_t s) {
   if (dt == MGG_BF16) return launch_tile<VAR, kBF16, kSfF32, kSfbBlock>(tile, p, s);
+  if (dt == MGG_FP8_FP4) return launch_tile<VAR, kFP4W, kSfUE8M0, kSfbBlock32>(tile, p, s);
   if (sf == MGG_SF_F32) {
     if (gran == MGG_SFB_BLOCK128) return launch_tile<VAR, kFP8, kSfF32, kSfbBlock>(tile, p, s);
     return launch_tile<VAR, kFP8, kSfF32, kSfbChannel>(tile, p, s);
@@ -182,21 +183,42 @@ uint32_t scale_bytes(long count, mgg_sf_fmt sf) {
 mgg_status check_common(mgg_dtype dt, int N, int K, const void* A, const void* SFA,
                         const void* B, const void* SFB, mgg_sf_fmt sf, const void* D,
                         const void* meta) {
-  if (dt != MGG_BF16 && dt != MGG_FP8_E4M3) return fail(MGG_EINVAL, "unknown dtype");
+  if (dt != MGG_BF16 && dt != MGG_FP8_E4M3 && dt != MGG_FP8_FP4)
+    return fail(MGG_EINVAL, "unknown dtype");
   if (N < 1 || N % 8 != 0) return fail(MGG_EINVAL, "N must be a positive multiple of 8");
   if (K < 1) return fail(MGG_EINVAL, "K must be positive");
   if (dt == MGG_BF16 && K % 8 != 0) return fail(MGG_EINVAL, "BF16 needs K % 8 == 0");
-  if (dt == MGG_FP8_E4M3 && K % 128 != 0) return fail(MGG_EINVAL, "FP8 needs K % 128 == 0");
+  if (dt != MGG_BF16 && K % 128 != 0) return fail(MGG_EINVAL, "FP8 needs K % 128 == 0");
   if (K > (1 << 28)) return fail(MGG_EUNSUPPORTED, "K too large");
   if (!A || !B || !D || !meta) return fail(MGG_EINVAL, "null pointer");
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16))
     return fail(MGG_EINVAL, "A, B and D must be 16-byte aligned");
-  if (dt == MGG_FP8_E4M3) {
+  if (dt != MGG_BF16) {
     if (!SFA || !SFB) return fail(MGG_EINVAL, "FP8 needs SFA and SFB");
     if (sf != MGG_SF_F32 && sf != MGG_SF_UE8M0) return fail(MGG_EINVAL, "unknown scale format");
     if (!aligned(SFA, 4) || !aligned(SFB, 4)) return fail(MGG_EINVAL, "scales must be 4-byte aligned");
+    if (dt == MGG_FP8_FP4 && sf != MGG_SF_UE8M0)
+      return fail(MGG_EUNSUPPORTED, "FP8 x FP4 takes UE8M0 scales");
   }
   if (!aligned(meta, 4)) return fail(MGG_EINVAL, "routing buffer must be 4-byte aligned");
+  return MGG_OK;
+}
+
+// Weight-scale entries of an M-grouped call and weight bytes per row, after checking
+// that the weight-scale granularity fits the element type.
+mgg_status weight_layout(mgg_dtype dt, mgg_sfb_gran gran, long G, long N, long K, long* sfb_n,
+                         long* b_row) {
+  const long KB = K / 128, NB = cdiv(N, 128);
+  *b_row = dt == MGG_BF16 ? 2 * K : (dt == MGG_FP8_FP4 ? K / 2 : K);
+  *sfb_n = 0;
+  if (dt == MGG_FP8_E4M3) {
+    if (gran == MGG_SFB_BLOCK128) *sfb_n = G * NB * KB;
+    else if (gran == MGG_SFB_CHANNEL) *sfb_n = G * KB * N;
+    else return fail(MGG_EINVAL, "unknown weight-scale granularity");
+  } else if (dt == MGG_FP8_FP4) {
+    if (gran != MGG_SFB_BLOCK32) return fail(MGG_EINVAL, "FP4 weights take MGG_SFB_BLOCK32 scales");
+    *sfb_n = G * KB * N * 4;
+  }
   return MGG_OK;
 }
 
@@ -264,12 +286,12 @@ mgg_status grouped_gemm_masked(mgg_dtype dt, int G, int cap, int N, int K, const
   if (st != MGG_OK) return st;
   if (G < 1 || G > kMaxExperts) return fail(MGG_EINVAL, "G must be in [1, 4096]");
   if (cap < 1) return fail(MGG_EINVAL, "cap must be positive");
-  if (dt == MGG_FP8_E4M3 && gran != MGG_SFB_BLOCK128 && gran != MGG_SFB_CHANNEL)
-    return fail(MGG_EINVAL, "unknown weight-scale granularity");
-  const long esz = dt == MGG_FP8_E4M3 ? 1 : 2, KB = K / 128, NB = cdiv(N, 128);
+  long sfb_n, b_row;
+  st = weight_layout(dt, gran, G, N, K, &sfb_n, &b_row);
+  if (st != MGG_OK) return st;
+  const long esz = dt == MGG_BF16 ? 2 : 1, KB = K / 128;
   const long sfa_n = (long)G * KB * cap;
-  const long sfb_n = gran == MGG_SFB_BLOCK128 ? (long)G * NB * KB : (long)G * KB * N;
-  st = check_sizes({(long)cap * K * esz, (long)N * K * esz, (long)cap * N * 2, sfa_n * 4,
+  st = check_sizes({(long)cap * K * esz, (long)N * b_row, (long)cap * N * 2, sfa_n * 4,
                     sfb_n * 4, (long)G * cdiv(cap, 32) * cdiv(N, 64)});
   if (st != MGG_OK) return st;
   Params p{};
@@ -283,8 +305,8 @@ mgg_status grouped_gemm_masked(mgg_dtype dt, int G, int cap, int N, int K, const
   p.rows = cap;
   p.N = N;
   p.K = K;
-  p.sfa_bytes = dt == MGG_FP8_E4M3 ? scale_bytes(sfa_n, sf) : 0;
-  p.sfb_bytes = dt == MGG_FP8_E4M3 ? scale_bytes(sfb_n, sf) : 0;
+  p.sfa_bytes = dt != MGG_BF16 ? scale_bytes(sfa_n, sf) : 0;
+  p.sfb_bytes = dt != MGG_BF16 ? scale_bytes(sfb_n, sf) : 0;
   p.meta_bytes = (uint32_t)G * 4;
   return dispatch_m<kMasked>(dt, sf, gran, pick_tile(expected_m, cap), p, stream);
 }
@@ -300,12 +322,12 @@ mgg_status grouped_gemm_contiguous(mgg_dtype dt, int G, int M, int N, int K, con
   if (G < 1 || G > kMaxExperts) return fail(MGG_EINVAL, "G must be in [1, 4096]");
   if (M < 1 || M > kMaxContigBlocks * kContigBlock)
     return fail(M < 1 ? MGG_EINVAL : MGG_EUNSUPPORTED, "M must be in [1, 524288]");
-  if (dt == MGG_FP8_E4M3 && gran != MGG_SFB_BLOCK128 && gran != MGG_SFB_CHANNEL)
-    return fail(MGG_EINVAL, "unknown weight-scale granularity");
-  const long esz = dt == MGG_FP8_E4M3 ? 1 : 2, KB = K / 128, NB = cdiv(N, 128);
+  long sfb_n, b_row;
+  st = weight_layout(dt, gran, G, N, K, &sfb_n, &b_row);
+  if (st != MGG_OK) return st;
+  const long esz = dt == MGG_BF16 ? 2 : 1, KB = K / 128;
   const long sfa_n = KB * M;
-  const long sfb_n = gran == MGG_SFB_BLOCK128 ? (long)G * NB * KB : (long)G * KB * N;
-  st = check_sizes({(long)M * K * esz, (long)N * K * esz, (long)M * N * 2, sfa_n * 4, sfb_n * 4});
+  st = check_sizes({(long)M * K * esz, (long)N * b_row, (long)M * N * 2, sfa_n * 4, sfb_n * 4});
   if (st != MGG_OK) return st;
   Params p{};
   p.A = (const uint8_t*)A;
@@ -318,8 +340,8 @@ mgg_status grouped_gemm_contiguous(mgg_dtype dt, int G, int M, int N, int K, con
   p.rows = M;
   p.N = N;
   p.K = K;
-  p.sfa_bytes = dt == MGG_FP8_E4M3 ? scale_bytes(sfa_n, sf) : 0;
-  p.sfb_bytes = dt == MGG_FP8_E4M3 ? scale_bytes(sfb_n, sf) : 0;
+  p.sfa_bytes = dt != MGG_BF16 ? scale_bytes(sfa_n, sf) : 0;
+  p.sfb_bytes = dt != MGG_BF16 ? scale_bytes(sfb_n, sf) : 0;
   p.meta_bytes = (uint32_t)M * 4;
   return dispatch_m<kContig>(dt, sf, gran, pick_tile(expected_m, kContigBlock), p, stream);
 }
@@ -334,12 +356,12 @@ mgg_status grouped_gemm_contiguous_psum(mgg_dtype dt, int G, int M, int N, int K
   if (st != MGG_OK) return st;
   if (G < 1 || G > kMaxExperts) return fail(MGG_EINVAL, "G must be in [1, 4096]");
   if (M < 1) return fail(MGG_EINVAL, "M must be positive");
-  if (dt == MGG_FP8_E4M3 && gran != MGG_SFB_BLOCK128 && gran != MGG_SFB_CHANNEL)
-    return fail(MGG_EINVAL, "unknown weight-scale granularity");
-  const long esz = dt == MGG_FP8_E4M3 ? 1 : 2, KB = K / 128, NB = cdiv(N, 128);
+  long sfb_n, b_row;
+  st = weight_layout(dt, gran, G, N, K, &sfb_n, &b_row);
+  if (st != MGG_OK) return st;
+  const long esz = dt == MGG_BF16 ? 2 : 1, KB = K / 128;
   const long sfa_n = KB * M;
-  const long sfb_n = gran == MGG_SFB_BLOCK128 ? (long)G * NB * KB : (long)G * KB * N;
-  st = check_sizes({(long)M * K * esz, (long)N * K * esz, (long)M * N * 2, sfa_n * 4, sfb_n * 4,
+  st = check_sizes({(long)M * K * esz, (long)N * b_row, (long)M * N * 2, sfa_n * 4, sfb_n * 4,
                     (cdiv(M, 32) + G) * cdiv(N, 64)});
   if (st != MGG_OK) return st;
   Params p{};
@@ -353,8 +375,8 @@ mgg_status grouped_gemm_contiguous_psum(mgg_dtype dt, int G, int M, int N, int K
   p.rows = M;
   p.N = N;
   p.K = K;
-  p.sfa_bytes = dt == MGG_FP8_E4M3 ? scale_bytes(sfa_n, sf) : 0;
-  p.sfb_bytes = dt == MGG_FP8_E4M3 ? scale_bytes(sfb_n, sf) : 0;
+  p.sfa_bytes = dt != MGG_BF16 ? scale_bytes(sfa_n, sf) : 0;
+  p.sfb_bytes = dt != MGG_BF16 ? scale_bytes(sfb_n, sf) : 0;
   p.meta_bytes = (uint32_t)G * 4;
   return dispatch_m<kPsum>(dt, sf, gran, pick_tile(expected_m, kContigBlock), p, stream);
 }
@@ -388,6 +410,7 @@ mgg_status kgrouped_impl(mgg_dtype dt, int G, int M, int N, int K_total, const v
   mgg_status st = check_common(dt, N, K_total > 0 ? K_total : (dt == MGG_FP8_E4M3 ? 128 : 8),
                                A, SFA, B, SFB, sf, D, ks);
   if (st != MGG_OK) return st;
+  if (dt == MGG_FP8_FP4) return fail(MGG_EUNSUPPORTED, "FP4 weights are M-grouped only");
   if (G < 1 || G > kMaxExperts) return fail(MGG_EINVAL, "G must be in [1, 4096]");
   if (M < 1) return fail(MGG_EINVAL, "M must be positive");
   if (accumulate != 0 && accumulate != 1) return fail(MGG_EINVAL, "accumulate must be 0 or 1");

@@ -34,7 +34,7 @@ struct TileCtx {
   int g;         // expert
   int m0, n0;    // first activation row / weight row of the tile
   int nk;        // 128-byte K slices to run (at least 1)
-  int k_bytes;   // bytes of K in every operand row (0: nothing to load)
+  int k_bytes;   // bytes of K in an activation row (0: nothing to load; FP4 weights: half)
   int a_lim;     // activation rows < a_lim are loaded (others read as zero)
   int row_end;   // masked: valid rows end; contiguous/K-grouped: M
   const uint8_t* a_base;  // expert's activation block
@@ -65,23 +65,29 @@ struct Sched {
 // instructions (1 KB for 16-byte copies, 256 B for 4-byte copies).
 template <class T, int VAR, int DT, int SF, int GRAN, bool ACC>
 struct Layout {
-  static constexpr bool FP8 = DT == kFP8;
+  static constexpr bool FP8 = DT != kBF16;  // scaled FP8 activations (FP8 or FP4 weights)
+  static constexpr bool FP4W = DT == kFP4W;
   static constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
-  static constexpr int AB_INSTR = (T::BM + T::BN) / 8;  // 8 rows of 128 B per copy
+  // Weight bytes per row per 128-K slice (FP4: two elements per byte).
+  static constexpr int B_ROW = FP4W ? kSliceBytes / 2 : kSliceBytes;
   // Scale runs: float32 -> one lane per scale; UE8M0 -> one lane per aligned dword of
   // the byte run (the run may start anywhere inside a dword).
   static constexpr int SA_LANES = FP8 ? (SF == kSfF32 ? T::BM : T::BM / 4 + 2) : 0;
   static constexpr int SBN_BLOCK = T::BN >= 128 ? T::BN / 128 : 1;
+  // FP4 weights: one dword per weight row per slice (its four 32-K block scales).
   static constexpr int SB_LANES =
-      FP8 ? (GRAN == kSfbChannel ? (SF == kSfF32 ? T::BN : T::BN / 4 + 2) : SBN_BLOCK) : 0;
+      FP4W ? T::BN
+           : FP8 ? (GRAN == kSfbChannel ? (SF == kSfF32 ? T::BN : T::BN / 4 + 2) : SBN_BLOCK)
+                 : 0;
   static constexpr int SA_INSTR = cdiv(SA_LANES, 64);
   static constexpr int SB_INSTR = cdiv(SB_LANES, 64);
   static constexpr int RI_INSTR = VAR == kContig ? cdiv(T::BM, 64) : 0;
   // Copy slots per wave. Operand rows: slot u of wave w copies rows 8(4u + w) ..
-  // 8(4u + w) + 7 of the [A; B] tile, so A and B slots are fixed per u (BM % 32 == 0).
+  // 8(4u + w) + 7 of the [A; B] tile, so A and B slots are fixed per u (BM % 32 == 0);
+  // FP4 weight rows are 64 bytes, so a weight slot covers 16 of them.
   // Scale and row-index copies are few: they are dealt to the four waves ("small"
   // slots, padded with a dummy copy).
-  static constexpr int U_A = T::BM / 32, U_B = T::BN / 32, U_AB = U_A + U_B;
+  static constexpr int U_A = T::BM / 32, U_B = T::BN * B_ROW / 4096, U_AB = U_A + U_B;
   static constexpr int SMALL = SA_INSTR + SB_INSTR + RI_INSTR;
   static constexpr int U_SM = cdiv(SMALL, 4);
   static constexpr int PER_WAVE = U_AB + U_SM;  // copy instructions per wave per item
@@ -89,7 +95,7 @@ struct Layout {
 
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = T::BM * kSliceBytes;
-  static constexpr int SA_OFF = B_OFF + T::BN * kSliceBytes;
+  static constexpr int SA_OFF = B_OFF + T::BN * B_ROW;
   static constexpr int SB_OFF = SA_OFF + SA_INSTR * 256;
   static constexpr int RI_OFF = SB_OFF + SB_INSTR * 256;
   static constexpr int DUMMY_OFF = RI_OFF + RI_INSTR * 256;
@@ -110,6 +116,10 @@ struct Layout {
   static constexpr int SCHED_OFF = PIPE + 2 * R_HALF;  // scheduler tables follow
 
   static_assert(FP8 || (T::WTM % 32 == 0 && T::WTN % 32 == 0), "BF16 needs 32x32 subtiles");
+  static_assert(!FP4W || (SF == kSfUE8M0 && GRAN == kSfbBlock32 && VAR != kKGrouped &&
+                          T::BN % 64 == 0),
+                "FP4 weights: UE8M0 scales applied by the MFMA, M-grouped, whole 16-row copies");
+  static_assert(FP4W == (GRAN == kSfbBlock32), "32-K weight scales go with FP4 weights");
   static_assert(PER_WAVE * (T::S - 1) <= 63, "vmcnt range of a copy wave");
   static_assert(!ACC || ((R_ROW_CHUNKS & (R_ROW_CHUNKS - 1)) == 0 && R_ROW_CHUNKS <= 64 &&
                          (T::BM * T::BN / 4) % 256 == 0),
@@ -229,7 +239,7 @@ __device__ __forceinline__ long first_tile() {
 template <class T, int VAR, int DT, int GRAN>
 __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Params& p, long& L) {
   TileCtx t = {};  // valid == 0, null bases: an idle cursor copies nothing
-  constexpr int esz = DT == kFP8 ? 1 : 2;
+  constexpr int esz = DT == kBF16 ? 2 : 1;  // activation bytes per element
   if constexpr (VAR == kMasked || VAR == kPsum) {
     if (L < S.total) {
       int lo = 0, hi = p.G - 1;  // largest g with prefix[g] <= L
@@ -255,11 +265,13 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       // masked: expert g's block of cap rows; psum: its segment of the [M] rows
       const long r0 = VAR == kPsum ? (long)S.s_c[g] : (long)g * p.rows;
       const long rn = VAR == kPsum ? (long)c : (long)p.rows;
+      const int Kbw = DT == kFP4W ? Kb / 2 : Kb;  // weight bytes per row
       t.a_base = p.A + r0 * Kb;
       t.a_bytes = (uint32_t)(rn * Kb);
-      t.b_base = p.B + (long)g * p.N * Kb;
-      t.b_bytes = (uint32_t)((long)p.N * Kb);
-      t.lda = t.ldb = Kb;
+      t.b_base = p.B + (long)g * p.N * Kbw;
+      t.b_bytes = (uint32_t)((long)p.N * Kbw);
+      t.lda = Kb;
+      t.ldb = Kbw;
       t.sfa_off = VAR == kPsum ? r0 : (long)g * KB * p.rows;
       t.sfa_ld = p.rows;
       if constexpr (GRAN == kSfbBlock) {
@@ -294,11 +306,13 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       t.nk = (Kb + kSliceBytes - 1) / kSliceBytes;
       t.a_lim = p.rows;
       t.row_end = p.rows;
+      const int Kbw = DT == kFP4W ? Kb / 2 : Kb;  // weight bytes per row
       t.a_base = p.A;
       t.a_bytes = (uint32_t)((long)p.rows * Kb);
-      t.b_base = p.B + (long)e * p.N * Kb;
-      t.b_bytes = (uint32_t)((long)p.N * Kb);
-      t.lda = t.ldb = Kb;
+      t.b_base = p.B + (long)e * p.N * Kbw;
+      t.b_bytes = (uint32_t)((long)p.N * Kbw);
+      t.lda = Kb;
+      t.ldb = Kbw;
       t.sfa_off = 0;
       t.sfa_ld = p.rows;
       if constexpr (GRAN == kSfbBlock) {
@@ -495,6 +509,14 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
       if (u < Lay::U_A) {
         const int m = t.m0 + R;
         I.vab[u] = (t.valid && m < t.a_lim) ? (uint32_t)(m * t.lda + c16) : kOOB;
+      } else if constexpr (Lay::FP4W) {
+        // 16 weight rows of 64 bytes per copy; chunk c of LDS row Rb sits at position
+        // c ^ ((Rb / 2) % 4), so 8 consecutive rows read at one logical chunk hit 8
+        // different 16-byte bank groups.
+        const int Rb = 16 * (4 * (u - Lay::U_A) + cwave) + (lane >> 2);
+        const int lc = (lane & 3) ^ ((Rb >> 1) & 3);
+        const int n = t.n0 + weight_row_of_lds<T, false>(Rb);
+        I.vab[u] = (t.valid && n < p.N) ? (uint32_t)(n * t.ldb + 16 * lc) : kOOB;
       } else {
         const int n = t.n0 + weight_row_of_lds<T, !FP8>(R - T::BM);
         I.vab[u] = (t.valid && n < p.N) ? (uint32_t)(n * t.ldb + c16) : kOOB;
@@ -513,8 +535,9 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
     dma_fence();
 #pragma unroll
     for (int u = 0; u < Lay::U_AB; ++u) {
-      uint32_t voff = I.vab[u] + kb0;
-      if (!full && kb0 + c16 + 16 > t.k_bytes) voff = kOOB;
+      // FP4 weight rows advance 64 bytes per slice (K is a multiple of 128: no tail)
+      uint32_t voff = I.vab[u] + (Lay::FP4W && u >= Lay::U_A ? s * Lay::B_ROW : kb0);
+      if (!Lay::FP4W && !full && kb0 + c16 + 16 > t.k_bytes) voff = kOOB;
       dma_x4(st + Lay::A_OFF + 1024 * (4 * u + cwave), u < Lay::U_A ? I.rs_a : I.rs_b, voff);
     }
 #pragma unroll
@@ -534,7 +557,10 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
         const int j = e - Lay::SA_INSTR;
         const int l = 64 * j + lane;
         uint32_t voff = kOOB;
-        if constexpr (GRAN == kSfbChannel) {
+        if constexpr (GRAN == kSfbBlock32) {  // one dword (four block scales) per row
+          const long o = t.sfb_off + (long)s * t.sfb_ld + t.n0;
+          if (t.valid && k_any && l < T::BN) voff = (uint32_t)((o + l) * 4);
+        } else if constexpr (GRAN == kSfbChannel) {
           const long o = t.sfb_off + (long)s * t.sfb_ld + t.n0;
           if constexpr (SF == kSfF32) {
             if (t.valid && k_any && l < T::BN) voff = (uint32_t)((o + l) * 4);
@@ -563,6 +589,7 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
   // ---- per-lane constant LDS offsets of the MFMA fragments (XOR swizzle folded in)
   const int x_lo = ((lg) ^ (lr & 7)) << 4;
   const int x_hi = ((lg + 4) ^ (lr & 7)) << 4;
+  const int x_w4 = (lg ^ ((lr >> 1) & 3)) << 4;  // FP4 weight rows (16 | R - lr)
 
   constexpr int NI2 = T::NI2, MJ2 = T::MJ2;
   v4f acc[FP8 ? NI : 1][FP8 ? MJ : 1];     // FP8: 16x16 subtiles
@@ -572,8 +599,10 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
   auto compute = [&](const TileCtx& t, int s, int stg) {
     const uint8_t* st = smem + stg * Lay::STAGE;
     if constexpr (FP8 && SF == kSfUE8M0) {
+      constexpr int kFmtW = Lay::FP4W ? 4 : 0;  // weight operand format: E2M1 or E4M3
       // Power-of-two scales: the MFMA applies them itself (its E8M0 operand scales, one
-      // per lane for the K elements that lane supplies, here all 128 of the slice) and
+      // per lane for the 32 K elements that lane supplies: activation and FP8 weight
+      // scales are the same across the slice, FP4 weight scales change every 32 K) and
       // accumulates into the tile accumulator, so no promotion instructions are needed:
       // the weight scale goes with the first operand (weight rows), the activation
       // scale with the second (activation rows).
@@ -598,14 +627,22 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
       // Weight fragment i and the scale of the weight row this lane supplies.
       auto load_w = [&](int i, v8i& afr, int& sb) {
         const int R = wn0 + 16 * i + lr;
-        const uint8_t* rp = st + Lay::B_OFF + R * kSliceBytes;
-        const v4i lo = *reinterpret_cast<const v4i*>(rp + x_lo);
-        const v4i hi = *reinterpret_cast<const v4i*>(rp + x_hi);
-        afr = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        sb = sbw;
-        if constexpr (GRAN == kSfbChannel) {
-          const long ob = t.sfb_off + (long)s * t.sfb_ld + t.n0;
-          sb = st[Lay::SB_OFF + (int)(ob & 3) + weight_row_of_lds<T, false>(R)];
+        if constexpr (Lay::FP4W) {
+          // 32 FP4 elements (K 32 lg .. 32 lg + 31) in the first four registers, and the
+          // scale of exactly that 32-K block of the weight row
+          const v4i q = *reinterpret_cast<const v4i*>(st + Lay::B_OFF + R * Lay::B_ROW + x_w4);
+          afr = (v8i){q.x, q.y, q.z, q.w, 0, 0, 0, 0};
+          sb = st[Lay::SB_OFF + 4 * weight_row_of_lds<T, false>(R) + lg];
+        } else {
+          const uint8_t* rp = st + Lay::B_OFF + R * kSliceBytes;
+          const v4i lo = *reinterpret_cast<const v4i*>(rp + x_lo);
+          const v4i hi = *reinterpret_cast<const v4i*>(rp + x_hi);
+          afr = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          sb = sbw;
+          if constexpr (GRAN == kSfbChannel) {
+            const long ob = t.sfb_off + (long)s * t.sfb_ld + t.n0;
+            sb = st[Lay::SB_OFF + (int)(ob & 3) + weight_row_of_lds<T, false>(R)];
+          }
         }
       };
       v8i wf[3];
@@ -618,7 +655,7 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
 #pragma unroll
         for (int j = 0; j < MJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              wf[i % 3], bfr[j], acc[i][j], 0, 0, 0, sw[i % 3], 0, sab[j]);
+              wf[i % 3], bfr[j], acc[i][j], kFmtW, 0, 0, sw[i % 3], 0, sab[j]);
       }
     } else if constexpr (FP8) {
       v8i bfr[MJ];

@@ -23,6 +23,11 @@ Recipes, each from the DeepGEMM pages the workloads come from:
 * Power-of-two (UE8M0) scales, "2^k" in the SM120 issue's environment section. The
   rounding rule is not printed there; the reading taken is the smallest power of two not
   below amax / 448 (so no code saturates), and 2^0 for a zero amax.
+* FP4 weights for the FP8 x FP4 products (the "fp8_fp4" kernel family the SM120 issue
+  names): E2M1 codes, two per byte with the even K element in the low nibble, one UE8M0
+  scale per weight row and 32-K block, the smallest power of two not below amax / 6 (6
+  being the largest E2M1 magnitude), codes = round-to-nearest-even of x / scale on the
+  E2M1 grid; scales stored [K/128][N][4].
 """
 
 from __future__ import annotations
@@ -33,6 +38,8 @@ import numpy as np
 import torch
 
 FP8_MAX = 448.0
+FP4_MAX = 6.0
+_E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
 GROUP = 128  # elements per scale along K (and rows per weight block)
 SENTINEL_BF16 = 0xDEAD  # bit pattern pre-filled into outputs to detect stray writes
 
@@ -115,6 +122,37 @@ def quant_weight_channel(w: torch.Tensor, sf_fmt: str = "f32"):
     return codes, sf
 
 
+def _to_e2m1(y: torch.Tensor) -> torch.Tensor:
+    """float32 values with |y| <= 6 -> E2M1 codes 0..15 (nearest grid point, ties to the
+    even code), as uint8."""
+    grid = torch.tensor(_E2M1_GRID, dtype=torch.float32, device=y.device)
+    a = y.abs().clamp(max=FP4_MAX)
+    hi = torch.bucketize(a, grid, right=False).clamp(max=len(_E2M1_GRID) - 1)  # grid[hi] >= a
+    lo = (hi - 1).clamp(min=0)
+    d_lo, d_hi = a - grid[lo], grid[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = torch.where(pick_hi, hi, lo)
+    code = code | (torch.signbit(y).to(code.dtype) << 3)
+    return code.to(torch.uint8)
+
+
+def quant_weight_fp4_block32(w: torch.Tensor):
+    """Weight w[N, K] -> (packed E2M1 bytes [N, K/2], UE8M0 scales [K/128, N, 4])."""
+    N, K = w.shape
+    assert K % GROUP == 0, "FP4 weights need K % 128 == 0"
+    wv = w.float().view(N, K // 32, 32)
+    ratio = wv.abs().amax(dim=2) / FP4_MAX  # [N, K/32]
+    mant, exp = torch.frexp(ratio)
+    e = torch.where(mant == 0.5, exp - 1, exp)
+    e = torch.where(ratio == 0, torch.zeros_like(e), e)
+    code = (e + 127).clamp(0, 254)
+    sf = torch.ldexp(torch.ones_like(ratio), code - 127)
+    c = _to_e2m1(wv / sf.unsqueeze(2)).view(N, K)
+    packed = (c[:, 0::2] | (c[:, 1::2] << 4)).contiguous()
+    scales = code.to(torch.uint8).view(N, K // GROUP, 4).permute(1, 0, 2).contiguous()
+    return packed, scales
+
+
 def quant_tokens_per_channel(x: torch.Tensor, sf_val: float = 1.0):
     """The K-grouped repro's cast: x[T, C] (tokens x channels) -> (codes [T, C],
     scales float32 [T/128, C]); a channel whose 128-token group is all zero gets sf_val."""
@@ -180,6 +218,13 @@ class Problem:
 
 def _weights(dtype, G, N, K, gen, device, sf_fmt, sfb_gran, std=1.0):
     """Per-expert weights B[G, N, K] and their scales, generated expert by expert."""
+    if dtype == "fp8_fp4":
+        assert sfb_gran == "block32"
+        B = torch.empty((G, N, K // 2), dtype=torch.uint8, device=device)
+        SFB = torch.empty((G, K // GROUP, N, 4), dtype=torch.uint8, device=device)
+        for g in range(G):
+            B[g], SFB[g] = quant_weight_fp4_block32(randn((N, K), 0, device, std, gen=gen))
+        return B, SFB
     if dtype == "bf16":
         B = torch.empty((G, N, K), dtype=torch.bfloat16, device=device)
         for g in range(G):
@@ -352,6 +397,16 @@ WORKLOADS = {
                                   K=7168, lam=192, expected_m=192, seed=4),
     "masked_fp8_g6_n4096": dict(variant="masked", dtype="fp8", G=6, cap=4096, N=4096,
                                 K=4096, lam=1024, expected_m=1024, seed=5),
+    # FP8 activations x FP4 weights (1x32 UE8M0 weight scales) on the same shapes
+    "contig_fp4_w13": dict(variant="contiguous", dtype="fp8_fp4", G=288, N=512, K=4096,
+                           lam=113, expected_m=113, seed=2, sf_fmt="ue8m0",
+                           sfb_gran="block32", rows_per_expert_max=256),
+    "contig_fp4_w2": dict(variant="contiguous", dtype="fp8_fp4", G=288, N=4096, K=256,
+                          lam=113, expected_m=113, seed=3, sf_fmt="ue8m0",
+                          sfb_gran="block32", rows_per_expert_max=256),
+    "masked_fp4_g6_n4096": dict(variant="masked", dtype="fp8_fp4", G=6, cap=4096, N=4096,
+                                K=4096, lam=1024, expected_m=1024, seed=5, sf_fmt="ue8m0",
+                                sfb_gran="block32"),
     "masked_bf16_g6_n4096": dict(variant="masked", dtype="bf16", G=6, cap=4096, N=4096,
                                  K=4096, lam=1024, expected_m=1024, seed=5),
 }

@@ -13,7 +13,10 @@ from the stated acceptance bar):
     on FP32 accumulation over K products plus the per-128-K promotion roundings. The
     third covers the FP8 MFMA's own sum of 128 products, whose internal precision is
     not published: measured on gfx950 it errs by up to about 1.3e-5 of that block's
-    sum of |products| (roughly 2^-16); 2^-14 of S keeps a 4x margin.
+    sum of |products| (roughly 2^-16); 2^-14 of S keeps a 4x margin. With FP4 weights
+    each 32-K block carries its own scale inside one instruction; a probe with block
+    scales spread over 15 binades measured up to 1.0e-4 of the sum of |products|, so
+    that dtype takes 2^-12 (2.4x margin over that extreme).
 """
 
 from __future__ import annotations
@@ -43,9 +46,14 @@ def np_codes(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
-def abs_codes(codes: np.ndarray, dtype: str) -> np.ndarray:
-    """Sign bit cleared: decodes to |value| for both element formats."""
-    return codes & (np.uint16(0x7FFF) if dtype == "bf16" else np.uint8(0x7F))
+def abs_codes(codes: np.ndarray, dtype: str, weights: bool = False) -> np.ndarray:
+    """Sign bits cleared: decodes to |value| for every element format (packed FP4 weight
+    bytes carry two sign bits, bits 3 and 7)."""
+    if dtype == "bf16":
+        return codes & np.uint16(0x7FFF)
+    if dtype == "fp8_fp4" and weights:
+        return codes & np.uint8(0x77)
+    return codes & np.uint8(0x7F)
 
 
 def sentinel_like(shape, device) -> torch.Tensor:
@@ -60,10 +68,14 @@ def tol(dtype: str) -> float:
     return 1e-5 if dtype == "bf16" else 1e-3
 
 
+# error of the scaled MFMA's own sum of 128 products, relative to their sum of |products|
+MFMA_BLOCK_REL = {"bf16": 0.0, "fp8": 2.0 ** -14, "fp8_fp4": 2.0 ** -12}
+
+
 def elementwise_ok(gpu: np.ndarray, ref: np.ndarray, S: np.ndarray, K: int, rounded: bool,
-                   fp8: bool):
+                   dtype: str):
     bound = ((2.0 ** -8 * np.abs(ref) if rounded else 0.0) + 1.25 * K * 2.0 ** -24 * S
-             + (2.0 ** -14 * S if fp8 else 0.0) + 1e-30)
+             + MFMA_BLOCK_REL[dtype] * S + 1e-30)
     err = np.abs(gpu - ref)
     bad = ~(err <= bound)
     return int(bad.sum()), float(np.max(err / bound)) if err.size else 0.0
@@ -93,7 +105,7 @@ def oracle_masked_expert(p: synth.Problem, g: int, rows=None, cols=None, host=No
     rr = None if rows is None else {0: rows}
     ref, valid = oracle.grouped_gemm_masked(p.dtype, A, B, cnt, SFA, SFB, p.sfb_gran, p.sf_fmt,
                                             experts=[0], rows=rr, cols=cols)
-    S, _ = oracle.grouped_gemm_masked(p.dtype, abs_codes(A, p.dtype), abs_codes(B, p.dtype), cnt,
+    S, _ = oracle.grouped_gemm_masked(p.dtype, abs_codes(A, p.dtype), abs_codes(B, p.dtype, True), cnt,
                                       SFA, SFB, p.sfb_gran, p.sf_fmt, experts=[0], rows=rr,
                                       cols=cols)
     return ref[0], S[0], valid[0]
@@ -119,7 +131,7 @@ def check_masked(p: synth.Problem, D: torch.Tensor, experts=None, rows=None, col
         gpu = oracle.decode_bf16(Dh[g][np.ix_(sel_rows, cc)])
         r = ref[np.ix_(sel_rows, cc)]
         s = S[np.ix_(sel_rows, cc)]
-        nb, w = elementwise_ok(gpu, r, s, p.K, rounded=True, fp8=p.dtype == "fp8")
+        nb, w = elementwise_ok(gpu, r, s, p.K, rounded=True, dtype=p.dtype)
         n_bad += nb
         worst = max(worst, w)
         all_gpu.append(gpu.ravel())
@@ -173,11 +185,11 @@ def check_contiguous(p: synth.Problem, D: torch.Tensor, rows=None, cols=None,
         ref, _ = oracle.grouped_gemm_contiguous(p.dtype, A[r_idx], B, sub_idx, sfa, SFB,
                                                 p.sfb_gran, p.sf_fmt, cols=cc)
         S, _ = oracle.grouped_gemm_contiguous(p.dtype, abs_codes(A[r_idx], p.dtype),
-                                              abs_codes(B, p.dtype), sub_idx, sfa, SFB,
+                                              abs_codes(B, p.dtype, True), sub_idx, sfa, SFB,
                                               p.sfb_gran, p.sf_fmt, cols=cc)
         ref, S = ref[:, cc], S[:, cc]
         gpu = oracle.decode_bf16(Dh[np.ix_(r_idx, cc)])
-        nb, w = elementwise_ok(gpu, ref, S, p.K, rounded=True, fp8=p.dtype == "fp8")
+        nb, w = elementwise_ok(gpu, ref, S, p.K, rounded=True, dtype=p.dtype)
         n_bad += nb
         worst = max(worst, w)
         all_gpu.append(gpu.ravel())
@@ -224,7 +236,7 @@ def check_kgrouped(p: synth.Problem, D: torch.Tensor, C=None, experts=None, rows
         r = ref[e][np.ix_(rr, cc)]
         s = S[e][np.ix_(rr, cc)]
         nb, w = elementwise_ok(gpu, r, s, max(ks[e], 1) + 2, rounded=False,
-                              fp8=p.dtype == "fp8")
+                              dtype=p.dtype)
         n_bad += nb
         worst = max(worst, w)
         all_gpu.append(gpu.ravel())
@@ -256,10 +268,10 @@ def check_psum(p: synth.Problem, D: torch.Tensor, psum=None, check_sentinel=True
     ref, valid = oracle.grouped_gemm_contiguous_psum(p.dtype, A, B, ps, SFA, SFB, p.sfb_gran,
                                                      p.sf_fmt)
     S, _ = oracle.grouped_gemm_contiguous_psum(p.dtype, abs_codes(A, p.dtype),
-                                               abs_codes(B, p.dtype), ps, SFA, SFB, p.sfb_gran,
+                                               abs_codes(B, p.dtype, True), ps, SFA, SFB, p.sfb_gran,
                                                p.sf_fmt)
     gpu = oracle.decode_bf16(Dh[valid])
-    nb, w = elementwise_ok(gpu, ref[valid], S[valid], p.K, rounded=True, fp8=p.dtype == "fp8")
+    nb, w = elementwise_ok(gpu, ref[valid], S[valid], p.K, rounded=True, dtype=p.dtype)
     diff = oracle.calc_diff(gpu, oracle.decode_bf16(oracle.round_to_bf16(ref[valid])))
     stray = int((Dh[~valid] != SENTINEL).sum()) if check_sentinel else 0
     return {"calc_diff": diff, "n_bad": nb, "worst": w, "stray": stray}

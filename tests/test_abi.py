@@ -110,6 +110,26 @@ def test_masked_rejects(lib, kw, code):
 
 
 @pytest.mark.parametrize("kw,code", [
+    (dict(dt=2, sf=0, gran=2), EUNSUPPORTED),  # FP8 x FP4 needs UE8M0 scales
+    (dict(dt=2, sf=1, gran=0), EINVAL),  # FP4 weights take 32-K block scales
+    (dict(dt=2, sf=1, gran=1), EINVAL),
+    (dict(dt=1, sf=1, gran=2), EINVAL),  # 32-K block scales go with FP4 weights only
+    (dict(dt=2, sf=1, gran=2, K=64), EINVAL),
+    (dict(dt=2, sf=1, gran=2, SFB=NUL), EINVAL),
+    (dict(dt=3), EINVAL),
+])
+def test_fp4_rejects(lib, kw, code):
+    assert masked(lib, **kw) == code
+    assert contig(lib, **kw) == code
+    assert psum_contig(lib, **kw) == code
+
+
+def test_fp4_kgrouped_unsupported(lib):
+    assert kgrp(lib, dt=2, sf=1) == EUNSUPPORTED
+    assert kgrp_psum(lib, dt=2, sf=1) == EUNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,code", [
     (dict(M=0), EINVAL),
     (dict(M=524289), EUNSUPPORTED),
     (dict(G=0), EINVAL),
