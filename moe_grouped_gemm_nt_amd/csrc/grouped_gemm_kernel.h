@@ -799,6 +799,19 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
             acc2[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[h & 1][i], bf[h & 1][j],
                                                                  acc2[i][j], 0, 0, 0);
       }
+      // Instruction order for the scheduler: the first step's reads, then each MFMA
+      // followed by one read of the next step's fragments.
+      {
+        constexpr int kReads = MJ2 + NI2;
+        __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);  // LDS reads
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+          for (int q = 0; q < NI2 * MJ2; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            if (h + 1 < 4 && q < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+      }
     }
   };
 
