@@ -250,6 +250,41 @@ mgg_status quantize_fp8_1x128(int M, int K, const void* X, void* Q, void* SF, mg
 mgg_status swiglu_quant_fp8_1x128(int M, int I, const void* H, void* Q, void* SF,
                                   mgg_sf_fmt sf, float sf_zero, hipStream_t stream);
 
+/*
+ * Contiguous FP8 GEMM with the SwiGLU + FP8 re-quantization fused into its epilogue: the
+ * w13 GEMM of the expert chain in the DeepGEMM issue "SM120 m_grouped_fp8 contiguous
+ * kernel: illegal memory access at CUDA graph replay" (sections "Environment" and "What
+ * works") followed by the step swiglu_quant_fp8_1x128 performs, without the bf16
+ * intermediate ever reaching memory. For each routed row r (expert e = m_indices[r], the
+ * contiguous rule of grouped_gemm_contiguous) and output column i < I:
+ *   h[r, c] = bf16(sum_k A[r, k] * B[e, c, k]) for c = i (gate) and c = I + i (up),
+ *   Q[r, i], SFQ[i / 128, r] = the 1x128 quantization of silu(h[r, i]) * h[r, I + i]
+ * exactly as swiglu_quant_fp8_1x128 computes it on the bf16 output of
+ * grouped_gemm_contiguous (the codes and scales are bit-identical to running the two).
+ *
+ *   dt          MGG_FP8_E4M3 or MGG_FP8_FP4 (MGG_BF16: MGG_EUNSUPPORTED).
+ *   M, I, K     rows (<= 524288), output columns per row (positive multiple of 128), K
+ *               (positive multiple of 128).
+ *   A, SFA      [M][K] codes, [K/128][M] scales, as in grouped_gemm_contiguous.
+ *   B, SFB      the w13 weights in their usual layout [G][2I][K] (gate rows 0..I-1, up
+ *               rows I..2I-1; FP4: [G][2I][K/2]) with their scales: FP8 BLOCK128 (float32
+ *               or UE8M0) or CHANNEL with float32 scales; FP4 BLOCK32.
+ *   Q           E4M3 bytes [M][I], 16-byte aligned.
+ *   SFQ, sfq    [I/128][M] scales, float32 (4-byte aligned) or UE8M0 bytes.
+ *   sf_zero     positive finite scale for all-zero groups.
+ *   m_indices   as in grouped_gemm_contiguous; rows that are not routed keep their Q and
+ *               SFQ contents.
+ * Errors: as grouped_gemm_contiguous; MGG_EUNSUPPORTED for BF16 or FP8 CHANNEL weight
+ * scales in UE8M0.
+ */
+mgg_status grouped_gemm_contiguous_swiglu_quant(mgg_dtype dt, int G, int M, int I, int K,
+                                               const void* A, const void* SFA,
+                                               const void* B, const void* SFB,
+                                               mgg_sf_fmt sf, mgg_sfb_gran gran,
+                                               void* Q, void* SFQ, mgg_sf_fmt sfq,
+                                               float sf_zero, const int32_t* m_indices,
+                                               hipStream_t stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* mgg_status_string(mgg_status s);
 

@@ -17,6 +17,9 @@ Entry points (same names as the C functions):
                           psum=False)   (psum=True calls grouped_gemm_kgrouped_psum)
     quantize_fp8_1x128(X, Q=None, SF=None, sf_fmt="f32", sf_zero=1.0) -> (Q, SF)
     swiglu_quant_fp8_1x128(H, Q=None, SF=None, sf_fmt="f32", sf_zero=1.0) -> (Q, SF)
+    grouped_gemm_contiguous_swiglu_quant(A, B, m_indices, SFA, SFB, Q=None, SFQ=None,
+                                         sfq_fmt="ue8m0", sf_zero=1.0, sfb_gran=None)
+                                         -> (Q, SFQ)
 
 Element types: bfloat16 tensors select BF16; uint8 (or float8_e4m3fn) tensors select
 FP8 E4M3; FP8 activations with weights of K/2 bytes per row (uint8 or float4_e2m1fn_x2)
@@ -37,6 +40,7 @@ __all__ = [
     "grouped_gemm_kgrouped",
     "quantize_fp8_1x128",
     "swiglu_quant_fp8_1x128",
+    "grouped_gemm_contiguous_swiglu_quant",
     "library_path",
     "load_library",
     "MggError",
@@ -83,10 +87,13 @@ def load_library() -> ctypes.CDLL:
     lib.grouped_gemm_kgrouped_psum.argtypes = list(lib.grouped_gemm_kgrouped.argtypes)
     lib.quantize_fp8_1x128.argtypes = [i32, i32, vp, vp, vp, i32, ctypes.c_float, st]
     lib.swiglu_quant_fp8_1x128.argtypes = list(lib.quantize_fp8_1x128.argtypes)
+    lib.grouped_gemm_contiguous_swiglu_quant.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp,
+                                                         vp, i32, i32, vp, vp, i32,
+                                                         ctypes.c_float, vp, st]
     for f in (lib.grouped_gemm_masked, lib.grouped_gemm_contiguous,
               lib.grouped_gemm_contiguous_psum, lib.grouped_gemm_kgrouped,
               lib.grouped_gemm_kgrouped_psum, lib.quantize_fp8_1x128,
-              lib.swiglu_quant_fp8_1x128):
+              lib.swiglu_quant_fp8_1x128, lib.grouped_gemm_contiguous_swiglu_quant):
         f.restype = ctypes.c_int
     lib.mgg_status_string.argtypes = [ctypes.c_int]
     lib.mgg_status_string.restype = ctypes.c_char_p
@@ -228,6 +235,42 @@ def grouped_gemm_contiguous_psum(A, B, D, psum, SFA=None, SFB=None, sfb_gran=Non
                                                 _ptr(D), _ptr(psum), int(expected_m),
                                                 _stream(A.device)))
     return D
+
+
+def grouped_gemm_contiguous_swiglu_quant(A, B, m_indices, SFA, SFB, Q=None, SFQ=None,
+                                         sfq_fmt="ue8m0", sf_zero=1.0, sfb_gran=None):
+    """The contiguous FP8 GEMM with the SwiGLU + 1x128 re-quantization in its epilogue:
+    A[M, K] FP8 codes, B[G, 2I, K] (FP4: [G, 2I, K/2]) w13 weights (gate rows, then up
+    rows) -> (Q uint8 [M, I] E4M3 codes, SFQ [I/128, M] float32 or uint8 UE8M0); Q and SFQ
+    are allocated when not given; rows that are not routed keep their contents."""
+    import torch
+    lib = load_library()
+    M, K = A.shape
+    G, N2, _ = B.shape
+    dt, gran = _m_operands(A, B, K)
+    _require(N2 % 2 == 0, "B must hold 2I rows")
+    I = N2 // 2
+    if Q is None:
+        Q = torch.empty((M, I), dtype=torch.uint8, device=A.device)
+    if SFQ is None:
+        SFQ = torch.empty((I // 128, M), device=A.device,
+                          dtype=torch.float32 if sfq_fmt == "f32" else torch.uint8)
+    _same_device(A, B, m_indices, SFA, SFB, Q, SFQ)
+    _contig(A, B, m_indices, SFA, SFB, Q, SFQ)
+    _require(tuple(Q.shape) == (M, I) and Q.dtype in (torch.uint8, torch.float8_e4m3fn),
+             "Q must be uint8 [M, I]")
+    _require(tuple(SFQ.shape) == (I // 128, M), "SFQ must be [I/128, M]")
+    fmt = {"f32": MGG_SF_F32, "ue8m0": MGG_SF_UE8M0}[sfq_fmt]
+    _require((SFQ.dtype == torch.float32) == (fmt == MGG_SF_F32), "SFQ dtype must match sfq_fmt")
+    _require(m_indices.dtype == torch.int32 and m_indices.numel() == M,
+             "m_indices must be int32 [M]")
+    sfb_gran = sfb_gran or gran
+    with torch.cuda.device(A.device):
+        _check(lib.grouped_gemm_contiguous_swiglu_quant(
+            dt, G, M, I, K, _ptr(A), _ptr(SFA), _ptr(B), _ptr(SFB), _sf_fmt(SFA),
+            _GRAN[sfb_gran], _ptr(Q), _ptr(SFQ), fmt, float(sf_zero), _ptr(m_indices),
+            _stream(A.device)))
+    return Q, SFQ
 
 
 def grouped_gemm_kgrouped(A, B, D, ks, M, N, SFA=None, SFB=None, accumulate=True,

@@ -78,16 +78,27 @@ struct Params {
   int accumulate;  // K-grouped: 1 adds the product to D
   int k_granule;   // K-grouped: required multiple of k_e (128 FP8, 8 BF16)
   int meta_psum;   // K-grouped: the routing holds cumulative token ends, not counts
+  // Fused SwiGLU epilogue (contiguous): D receives E4M3 codes [rows][N/2] of
+  // silu(gate) * up and SFQ their 1x128 scales [N/256][rows] (float32, or UE8M0 bytes
+  // when sfq_ue8m0); an all-zero group takes sf_zero.
+  void* SFQ;
+  int sfq_ue8m0;
+  float sf_zero;
+  uint32_t sfq_bytes;
   uint32_t sfa_bytes, sfb_bytes;  // readable bytes of the scale tensors (FP8)
   uint32_t meta_bytes;            // bytes of the routing tensor
 };
 
 // Tile configuration: BM activation rows x BN weight rows per workgroup; WM x WN MFMA
 // waves (four or eight) laid out WM along m and WN along n; S pipeline stages of
-// 128-byte K slices in LDS.
-template <int BM_, int BN_, int WM_, int WN_, int S_>
+// 128-byte K slices in LDS. SWI: the fused SwiGLU tile of the contiguous product, whose
+// 256 weight rows are the gate rows and then the up rows of 128 output columns, one
+// wave row-band covering all of them (so a row's 1x128 output group stays in one wave).
+template <int BM_, int BN_, int WM_, int WN_, int S_, bool SWI_ = false>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_;
+  static constexpr bool SWI = SWI_;
+  static_assert(!SWI || (BN == 256 && WN == 1), "fused SwiGLU tile: 256 weight rows, one wave column");
   static constexpr int NMW = WM * WN;  // MFMA waves
   static_assert(NMW == 4 || NMW == 8, "four or eight MFMA waves");
   static_assert(S >= 2 && S <= 6, "pipeline depth");
@@ -97,7 +108,8 @@ struct Tile {
   static constexpr int MJ = WTM / 16, NI = WTN / 16;
   static constexpr int MJ2 = WTM / 32, NI2 = WTN / 32;
   static_assert(MJ >= 1 && NI >= 2 && WTM % 16 == 0 && WTN % 16 == 0, "16x16 subtiles");
-  static_assert(WTN <= 128 && 128 % WTN == 0, "a wave's n range stays in one 128-row block");
+  static_assert(SWI || (WTN <= 128 && 128 % WTN == 0),
+                "a wave's n range stays in one 128-row block");
   static_assert((BM + BN) % 32 == 0 && BM % 8 == 0, "whole 8-row copies, 4 waves");
 };
 
@@ -298,6 +310,21 @@ extern "C" __device__ v4i mgg_raw_buffer_load_v4i32(v4i rsrc, int voffset, int s
 template <int AUX = kCacheDefault>
 __device__ __forceinline__ v4i load_b128(v4i rsrc, uint32_t voff) {
   return mgg_raw_buffer_load_v4i32(rsrc, (int)voff, 0, AUX);
+}
+
+// 4-byte and 1-byte stores (per-row scales of a fused epilogue).
+extern "C" __device__ void mgg_raw_buffer_store_i32(int vdata, v4i rsrc, int voffset,
+                                                    int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.store.i32");
+extern "C" __device__ void mgg_raw_buffer_store_i8(char vdata, v4i rsrc, int voffset,
+                                                   int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.store.i8");
+
+__device__ __forceinline__ void store_b32(v4i rsrc, uint32_t voff, uint32_t v) {
+  mgg_raw_buffer_store_i32((int)v, rsrc, (int)voff, 0, kCacheDefault);
+}
+__device__ __forceinline__ void store_b8(v4i rsrc, uint32_t voff, uint32_t v) {
+  mgg_raw_buffer_store_i8((char)v, rsrc, (int)voff, 0, kCacheDefault);
 }
 
 }  // namespace mgg

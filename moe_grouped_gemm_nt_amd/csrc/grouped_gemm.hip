@@ -37,6 +37,9 @@ using TileL = Tile<128, 256, 2, 2, 3>;   // larger experts, BF16
 // the K = 256 contiguous shape, whose tiles are mostly epilogue, and 2-4 % on the
 // MFMA-bound 6 x 4096 x 4096 shape; BF16 is better served by four)
 using TileL8 = Tile<128, 256, 2, 4, 3>;
+// the fused SwiGLU tile: 128 output columns (their gate and up weight rows), eight waves
+// of 16 rows x all 256 weight rows
+using TileSwi = Tile<128, 256, 8, 1, 3, true>;
 using TileK = Tile<64, 128, 2, 2, 3>;    // K-grouped output tiles
 
 enum TileId { kTileS = 0, kTileM = 1, kTileL = 2 };
@@ -384,6 +387,65 @@ mgg_status grouped_gemm_contiguous_psum(mgg_dtype dt, int G, int M, int N, int K
   p.sfb_bytes = dt != MGG_BF16 ? scale_bytes(sfb_n, sf) : 0;
   p.meta_bytes = (uint32_t)G * 4;
   return dispatch_m<kPsum>(dt, sf, gran, pick_tile(expected_m, kContigBlock), p, stream);
+}
+
+mgg_status grouped_gemm_contiguous_swiglu_quant(mgg_dtype dt, int G, int M, int I, int K,
+                                               const void* A, const void* SFA, const void* B,
+                                               const void* SFB, mgg_sf_fmt sf,
+                                               mgg_sfb_gran gran, void* Q, void* SFQ,
+                                               mgg_sf_fmt sfq, float sf_zero,
+                                               const int32_t* m_indices, hipStream_t stream) {
+  g_last_error.clear();
+  if (dt == MGG_BF16)
+    return fail(MGG_EUNSUPPORTED, "the fused SwiGLU epilogue takes FP8 activations");
+  if (I < 128 || I % 128 != 0) return fail(MGG_EINVAL, "I must be a positive multiple of 128");
+  if (I > (1 << 27)) return fail(MGG_EUNSUPPORTED, "I too large");
+  mgg_status st = check_common(dt, 2 * I, K, A, SFA, B, SFB, sf, Q, m_indices);
+  if (st != MGG_OK) return st;
+  if (G < 1 || G > kMaxExperts) return fail(MGG_EINVAL, "G must be in [1, 4096]");
+  if (M < 1 || M > kMaxContigBlocks * kContigBlock)
+    return fail(M < 1 ? MGG_EINVAL : MGG_EUNSUPPORTED, "M must be in [1, 524288]");
+  if (dt == MGG_FP8_E4M3 && gran == MGG_SFB_CHANNEL && sf == MGG_SF_UE8M0)
+    return fail(MGG_EUNSUPPORTED, "the fused SwiGLU epilogue takes UE8M0 weight scales per 128x128 block");
+  if (!SFQ) return fail(MGG_EINVAL, "null pointer");
+  if (sfq != MGG_SF_F32 && sfq != MGG_SF_UE8M0) return fail(MGG_EINVAL, "unknown scale format");
+  if (sfq == MGG_SF_F32 && !aligned(SFQ, 4))
+    return fail(MGG_EINVAL, "float32 output scales must be 4-byte aligned");
+  if (!(sf_zero > 0.f) || !(sf_zero < 3.0e38f))
+    return fail(MGG_EINVAL, "sf_zero must be a positive finite float");
+  long sfb_n, b_row;
+  st = weight_layout(dt, gran, G, 2L * I, K, &sfb_n, &b_row);
+  if (st != MGG_OK) return st;
+  const long KB = K / 128;
+  const long sfa_n = KB * M, sfq_n = (long)(I / 128) * M;
+  st = check_sizes({(long)M * K, 2L * I * b_row, (long)M * I, sfa_n * 4, sfb_n * 4, sfq_n * 4});
+  if (st != MGG_OK) return st;
+  Params p{};
+  p.A = (const uint8_t*)A;
+  p.B = (const uint8_t*)B;
+  p.SFA = SFA;
+  p.SFB = SFB;
+  p.D = Q;
+  p.meta = m_indices;
+  p.G = G;
+  p.rows = M;
+  p.N = 2 * I;
+  p.K = K;
+  p.sfa_bytes = scale_bytes(sfa_n, sf);
+  p.sfb_bytes = scale_bytes(sfb_n, sf);
+  p.meta_bytes = (uint32_t)M * 4;
+  p.SFQ = SFQ;
+  p.sfq_ue8m0 = sfq == MGG_SF_UE8M0;
+  p.sf_zero = sf_zero;
+  p.sfq_bytes = scale_bytes(sfq_n, sfq);
+  const long tiles = m_tiles<TileSwi, kContig>(p);
+  if (dt == MGG_FP8_FP4)
+    return launch<TileSwi, kContig, kFP4W, kSfUE8M0, kSfbBlock32, false>(p, tiles, stream);
+  if (sf == MGG_SF_UE8M0)
+    return launch<TileSwi, kContig, kFP8, kSfUE8M0, kSfbBlock, false>(p, tiles, stream);
+  if (gran == MGG_SFB_BLOCK128)
+    return launch<TileSwi, kContig, kFP8, kSfF32, kSfbBlock, false>(p, tiles, stream);
+  return launch<TileSwi, kContig, kFP8, kSfF32, kSfbChannel, false>(p, tiles, stream);
 }
 
 mgg_status grouped_gemm_kgrouped(mgg_dtype dt, int G, int M, int N, int K_total, const void* A,

@@ -24,6 +24,7 @@
 // that publishes the last exchange tile), so nothing else needs synchronising.
 #pragma once
 
+#include "act_math.h"
 #include "gemm_engine.h"
 
 namespace mgg {
@@ -323,7 +324,8 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
         t.sfb_ld = p.N;
       }
       t.d_base = reinterpret_cast<uint8_t*>(p.D);
-      t.d_bytes = (uint32_t)((long)p.rows * p.N * 2);
+      // bf16 [rows][N]; the fused SwiGLU tile writes E4M3 codes [rows][N/2]
+      t.d_bytes = (uint32_t)((long)p.rows * (T::SWI ? p.N / 2 : p.N * 2));
       break;
     }
   } else {
@@ -493,6 +495,19 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
   // ---- the issue cursor's per-tile copy state: resource descriptors and per-lane
   // byte offsets of every operand-row copy slot (kOOB for rows outside the tile's
   // valid range); a slice only adds its K offset.
+  // Global weight row of tile-local weight row w, and whether it exists. The fused
+  // SwiGLU tile's rows 0..127 are the gate rows of its 128 output columns and rows
+  // 128..255 the matching up rows, N / 2 further on.
+  auto weight_row = [&](const TileCtx& t, int w, int& n) -> bool {
+    if constexpr (T::SWI) {
+      const int oc = t.n0 / 2 + (w & 127);
+      n = (w < 128 ? 0 : p.N / 2) + oc;
+      return oc < p.N / 2;
+    } else {
+      n = t.n0 + w;
+      return n < p.N;
+    }
+  };
   struct Issue {
     TileCtx t;
     v4i rs_a, rs_b;
@@ -519,11 +534,13 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
         // different 16-byte bank groups.
         const int Rb = 16 * (4 * (u - Lay::U_A) + cwave) + (lane >> 2);
         const int lc = (lane & 3) ^ ((Rb >> 1) & 3);
-        const int n = t.n0 + weight_row_of_lds<T, false>(Rb);
-        I.vab[u] = (t.valid && n < p.N) ? (uint32_t)(n * t.ldb + 16 * lc) : kOOB;
+        int n;
+        const bool ok = weight_row(t, weight_row_of_lds<T, false>(Rb), n);
+        I.vab[u] = (t.valid && ok) ? (uint32_t)(n * t.ldb + 16 * lc) : kOOB;
       } else {
-        const int n = t.n0 + weight_row_of_lds<T, !FP8>(R - T::BM);
-        I.vab[u] = (t.valid && n < p.N) ? (uint32_t)(n * t.ldb + c16) : kOOB;
+        int n;
+        const bool ok = weight_row(t, weight_row_of_lds<T, !FP8>(R - T::BM), n);
+        I.vab[u] = (t.valid && ok) ? (uint32_t)(n * t.ldb + c16) : kOOB;
       }
     }
   };
@@ -561,18 +578,19 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
         const int j = e - Lay::SA_INSTR;
         const int l = 64 * j + lane;
         uint32_t voff = kOOB;
-        if constexpr (GRAN == kSfbBlock32) {  // one dword (four block scales) per row
-          const long o = t.sfb_off + (long)s * t.sfb_ld + t.n0;
-          if (t.valid && k_any && l < T::BN) voff = (uint32_t)((o + l) * 4);
+        if constexpr (GRAN == kSfbBlock32 || (GRAN == kSfbChannel && SF == kSfF32)) {
+          // one dword per weight row: four 32-K block scales, or one float32 scale
+          const long o = t.sfb_off + (long)s * t.sfb_ld;
+          int n;
+          const bool ok = l < T::BN && weight_row(t, l, n);
+          if (t.valid && k_any && ok) voff = (uint32_t)((o + n) * 4);
         } else if constexpr (GRAN == kSfbChannel) {
           const long o = t.sfb_off + (long)s * t.sfb_ld + t.n0;
-          if constexpr (SF == kSfF32) {
-            if (t.valid && k_any && l < T::BN) voff = (uint32_t)((o + l) * 4);
-          } else {
-            if (t.valid && k_any && l < Lay::SB_LANES) voff = (uint32_t)((o & ~3L) + 4 * l);
-          }
+          static_assert(!T::SWI, "byte-run channel scales are not gathered");
+          if (t.valid && k_any && l < Lay::SB_LANES) voff = (uint32_t)((o & ~3L) + 4 * l);
         } else {
-          const int nb = t.n0 / 128 + l;
+          // 128x128 blocks; the fused tile's two are its gate block and its up block
+          const int nb = T::SWI ? (l == 0 ? t.n0 / 256 : p.N / 256 + t.n0 / 256) : t.n0 / 128 + l;
           const long o = t.sfb_off + (long)nb * t.sfb_ld + s;
           if (t.valid && k_any && l < Lay::SBN_BLOCK && nb * 128 < p.N)
             voff = SF == kSfF32 ? (uint32_t)(o * 4) : (uint32_t)(o & ~3L);
@@ -622,11 +640,18 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
         bfr[j] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         sab[j] = st[Lay::SA_OFF + (int)(oa & 3) + row];
       }
-      int sbw = 0;
+      int sbw = 0, sbw2 = 0;  // block scale of the wave's rows (fused tile: gate, up)
       if constexpr (GRAN == kSfbBlock) {
-        const int lb = ((t.n0 & 127) + wn0) >> 7;
-        const long ob = t.sfb_off + (long)(t.n0 / 128 + lb) * t.sfb_ld + s;
-        sbw = st[Lay::SB_OFF + 4 * lb + (int)(ob & 3)];
+        if constexpr (T::SWI) {
+          const long og = t.sfb_off + (long)(t.n0 / 256) * t.sfb_ld + s;
+          const long ou = t.sfb_off + (long)(p.N / 256 + t.n0 / 256) * t.sfb_ld + s;
+          sbw = st[Lay::SB_OFF + (int)(og & 3)];
+          sbw2 = st[Lay::SB_OFF + 4 + (int)(ou & 3)];
+        } else {
+          const int lb = ((t.n0 & 127) + wn0) >> 7;
+          const long ob = t.sfb_off + (long)(t.n0 / 128 + lb) * t.sfb_ld + s;
+          sbw = st[Lay::SB_OFF + 4 * lb + (int)(ob & 3)];
+        }
       }
       // Weight fragment i and the scale of the weight row this lane supplies.
       auto load_w = [&](int i, v8i& afr, int& sb) {
@@ -642,7 +667,9 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
           const v4i lo = *reinterpret_cast<const v4i*>(rp + x_lo);
           const v4i hi = *reinterpret_cast<const v4i*>(rp + x_hi);
           afr = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-          sb = sbw;
+          // fused tile: LDS rows 16 i + lr hold weight rows 64 (lr / 4) + 4 i + lr % 4, so
+          // lanes lr >= 8 supply up rows
+          sb = (T::SWI && lr >= 8) ? sbw2 : sbw;
           if constexpr (GRAN == kSfbChannel) {
             const long ob = t.sfb_off + (long)s * t.sfb_ld + t.n0;
             sb = st[Lay::SB_OFF + (int)(ob & 3) + weight_row_of_lds<T, false>(R)];
@@ -693,12 +720,14 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
         else
           sa[j] = ue8m0_to_float(st[Lay::SA_OFF + (int)(oa & 3) + row]);
       }
-      float sbw = 0.f;
+      float sbw = 0.f, sbw2 = 0.f;  // block scale of the wave's rows (fused tile: gate, up)
       if constexpr (GRAN == kSfbBlock) {
         const int lb = ((t.n0 & 127) + wn0) >> 7;
         if constexpr (SF == kSfF32) {
-          sbw = reinterpret_cast<const float*>(st + Lay::SB_OFF)[lb];
+          sbw = reinterpret_cast<const float*>(st + Lay::SB_OFF)[T::SWI ? 0 : lb];
+          if constexpr (T::SWI) sbw2 = reinterpret_cast<const float*>(st + Lay::SB_OFF)[1];
         } else {
+          static_assert(!T::SWI || SF == kSfF32, "unreachable: UE8M0 takes the MFMA-scaled path");
           const long ob = t.sfb_off + (long)(t.n0 / 128 + lb) * t.sfb_ld + s;
           sbw = ue8m0_to_float(st[Lay::SB_OFF + 4 * lb + (int)(ob & 3)]);
         }
@@ -709,7 +738,11 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
         const v4i lo = *reinterpret_cast<const v4i*>(rp + x_lo);
         const v4i hi = *reinterpret_cast<const v4i*>(rp + x_hi);
         afr = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        sbv = (v4f){sbw, sbw, sbw, sbw};
+        {
+          // fused tile: this lane's output columns 64 lg + 4 i + r are up columns for lg >= 2
+          const float b = (T::SWI && lg >= 2) ? sbw2 : sbw;
+          sbv = (v4f){b, b, b, b};
+        }
         if constexpr (GRAN == kSfbChannel) {
           const int col = wn0 + lg * 4 * NI + 4 * i;
           if constexpr (SF == kSfF32) {
@@ -822,6 +855,61 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
     const uint8_t* st = smem + stg * Lay::STAGE;
     uint8_t* R = smem + Lay::R_OFF + rx;
     const v4i rs_d = make_rsrc(t.d_base, t.d_bytes);
+    if constexpr (T::SWI) {
+      // Fused SwiGLU + FP8 1x128 quantization of the tile's 128 output columns. Each
+      // accumulator is first rounded to bf16 (the value a separate GEMM would store), so
+      // the codes equal those of the separate SwiGLU kernel run on that output. Lane group
+      // g (lane / 16) holds tile columns 64 g .. 64 g + 63 of its row: gate columns for
+      // g < 2, the matching up columns for g >= 2 (lane + 32). The two lanes of a pair
+      // swap halves so that each ends with 32 gate and 32 up values of the same output
+      // columns: lane g < 2 computes outputs 64 g .. 64 g + 31, lane g + 2 outputs
+      // 64 g + 32 .. 64 g + 63. The row's maximum meets over the four lanes.
+      static_assert(MJ == 1 && NI == 16 && VAR == kContig, "fused tile: one 16-row band per wave");
+      const int rl = wm0 + lr;
+      const int m = t.m0 + rl;
+      const int I = p.N / 2, oc0 = t.n0 / 2;
+      bool row_ok = m < t.row_end && oc0 < I;
+      row_ok = row_ok && reinterpret_cast<const int*>(st + Lay::RI_OFF)[rl] == t.g;
+      const bool lo = lg < 2;
+      float x[8][4];
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float h0 = __uint_as_float(f32_to_bf16_rne(acc[i][0][r]) << 16);
+          const float h1 = __uint_as_float(f32_to_bf16_rne(acc[i + 8][0][r]) << 16);
+          const float other = __shfl_xor(lo ? h1 : h0, 32);  // the partner's half
+          const float gate = lo ? h0 : other, up = lo ? other : h1;
+          x[i][r] = silu_fixed(gate) * up;
+          amax = fmaxf(amax, fabsf(x[i][r]));
+        }
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      uint32_t bits;
+      const float inv = p.sfq_ue8m0 ? group_scale_1x128<true>(amax, p.sf_zero, bits)
+                                    : group_scale_1x128<false>(amax, p.sf_zero, bits);
+      const int col = oc0 + 64 * (lg & 1) + (lo ? 0 : 32);  // first output column of lane
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        v4i w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float* v = x[4 * q + e];
+          w[e] = (int)to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+        }
+        const uint32_t voff = row_ok ? (uint32_t)((long)m * I + col + 16 * q) : kOOB;
+        store_b128(rs_d, voff, w);
+      }
+      const v4i rs_q = make_rsrc(p.SFQ, p.sfq_bytes);
+      const long qi = (long)(oc0 / 128) * p.rows + m;
+      const bool wq = row_ok && lg == 0;
+      if (p.sfq_ue8m0)
+        store_b8(rs_q, wq ? (uint32_t)qi : kOOB, bits);
+      else
+        store_b32(rs_q, wq ? (uint32_t)(qi * 4) : kOOB, bits);
+      return;
+    }
     if constexpr (FP8) {
       const int nl0 = wn0 + lg * 4 * NI;  // tile-local first column of this lane
       const int n_start = t.n0 + nl0;

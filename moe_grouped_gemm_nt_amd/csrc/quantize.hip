@@ -26,9 +26,14 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include "act_math.h"
 #include "moe_grouped_gemm_nt.h"
 
 namespace {
+
+using mgg::group_scale_1x128;
+using mgg::silu_fixed;
+using mgg::to_e4m3x4;
 
 constexpr int kUnitsPerBlock = 64;  // (row, 128-column group) units: 16 quarters x 4 steps
 constexpr int kThreadsQ = 256;
@@ -38,64 +43,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Smallest u with 2^(u - 127) >= s (s > 0), from the float32 bits of s.
-__device__ __forceinline__ uint32_t ue8m0_at_least(float s) {
-  const uint32_t b = __float_as_uint(s);
-  return ((b >> 23) & 0xffu) + ((b & 0x7fffffu) != 0u ? 1u : 0u);
-}
-
-// Four float32 values -> four E4M3 codes (round to nearest even), packed little-endian.
-__device__ __forceinline__ uint32_t to_e4m3x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return (uint32_t)w;
-}
-
-// Taylor coefficients (ln 2)^k / k!, k = 0..7, of 2^r = e^(r ln 2): each built in double
-// as c_k = c_(k-1) * ln 2 / k and rounded once to float.
-struct ExpPoly {
-  float c[8];
-};
-constexpr ExpPoly make_exp_poly() {
-  ExpPoly p{};
-  double c = 1.0;
-  p.c[0] = 1.0f;
-  for (int k = 1; k < 8; ++k) {
-    c = c * 0.6931471805599453 / k;
-    p.c[k] = (float)c;
-  }
-  return p;
-}
-constexpr ExpPoly kExpPoly = make_exp_poly();
-
-// e^y as one fixed float32 evaluation, so that every rounding is specified: t = y log2(e)
-// (one float multiply), n = t rounded to the nearest integer (ties to even), r = t - n
-// (exact, |r| <= 1/2), 2^r by the degree-7 Taylor polynomial in Horner form with every
-// multiply and add rounded separately (contraction into fused multiply-adds is switched
-// off here), then an exact scaling by 2^n. t is clamped to [-150, 128]: above 128 the
-// result is +inf, below -150 it is 0. Relative error below 1e-5 on the range silu uses.
-__device__ __forceinline__ float exp_fixed(float y) {
-#pragma clang fp contract(off)
-  float t = y * (float)1.4426950408889634;
-  const bool big = t > 128.0f, small = t < -150.0f;
-  t = fminf(fmaxf(t, -150.0f), 128.0f);
-  const float n = __builtin_rintf(t);
-  const float r = t - n;
-  float p = kExpPoly.c[7];
-#pragma unroll
-  for (int k = 6; k >= 0; --k) p = p * r + kExpPoly.c[k];
-  float out = ldexpf(p, (int)n);
-  out = big ? __builtin_huge_valf() : out;
-  return small ? 0.0f : out;
-}
-
-// silu(x) = x / (1 + e^-x): one float add and one IEEE float division.
-__device__ __forceinline__ float silu_fixed(float x) {
-#pragma clang fp contract(off)
-  const float d = 1.0f + exp_fixed(-x);
-  return x / d;
-}
 
 // One workgroup covers 64 (row, 128-column group) units: GB = 2^gb_log groups side by
 // side (GB = 4 for rows of at least 512 columns, fewer for narrower rows so no lane idles)
@@ -150,19 +97,8 @@ __global__ __launch_bounds__(kThreadsQ) void quant_rows_1x128(const uint16_t* __
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
-    float s = amax / 448.0f;  // IEEE float32 division
-    float inv;
     uint32_t sfbits;
-    if constexpr (UE8M0) {
-      const uint32_t code = ue8m0_at_least(s == 0.f ? sf_zero : s);
-      inv = ldexpf(1.0f, 127 - (int)code);  // exact
-      sfbits = code;
-    } else {
-      if (s == 0.f) s = sf_zero;
-      s = fmaxf(s, 1e-30f);
-      inv = 1.0f / s;  // IEEE float32 division
-      sfbits = __float_as_uint(s);
-    }
+    const float inv = group_scale_1x128<UE8M0>(amax, sf_zero, sfbits);
     u32x2 out;
     out.x = to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
     out.y = to_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);

@@ -37,9 +37,10 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for f in ("grouped_gemm_masked", "grouped_gemm_contiguous", "grouped_gemm_contiguous_psum",
               "grouped_gemm_kgrouped", "grouped_gemm_kgrouped_psum", "quantize_fp8_1x128",
-              "swiglu_quant_fp8_1x128", "mgg_status_string", "mgg_last_error"):
+              "swiglu_quant_fp8_1x128", "grouped_gemm_contiguous_swiglu_quant",
+              "mgg_status_string", "mgg_last_error"):
         assert f in names
-    assert len(names) == 9, names
+    assert len(names) == 10, names
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -122,6 +123,38 @@ def test_fp4_rejects(lib, kw, code):
     assert masked(lib, **kw) == code
     assert contig(lib, **kw) == code
     assert psum_contig(lib, **kw) == code
+
+
+def fused(lib, dt=1, G=2, M=256, I=128, K=128, A=P, SFA=P, B=P, SFB=P, sf=1, gran=0, Q=P,
+          SFQ=P, sfq=1, z=1.0, idx=P):
+    return lib.grouped_gemm_contiguous_swiglu_quant(dt, G, M, I, K, A, SFA, B, SFB, sf, gran, Q,
+                                                    SFQ, sfq, ctypes.c_float(z), idx, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=0), EUNSUPPORTED),
+    (dict(dt=3), EINVAL),
+    (dict(I=0), EINVAL),
+    (dict(I=192), EINVAL),
+    (dict(K=64), EINVAL),
+    (dict(G=0), EINVAL),
+    (dict(M=0), EINVAL),
+    (dict(M=524289), EUNSUPPORTED),
+    (dict(Q=NUL), EINVAL),
+    (dict(Q=MIS), EINVAL),
+    (dict(SFQ=NUL), EINVAL),
+    (dict(sfq=0, SFQ=ctypes.c_void_p((1 << 20) + 2)), EINVAL),
+    (dict(sfq=4), EINVAL),
+    (dict(z=0.0), EINVAL),
+    (dict(z=float("nan")), EINVAL),
+    (dict(idx=NUL), EINVAL),
+    (dict(sf=1, gran=1), EUNSUPPORTED),  # byte-run channel scales are not gathered
+    (dict(dt=2, sf=1, gran=0), EINVAL),  # FP4 weights take 32-K block scales
+    (dict(dt=2, sf=0, gran=2), EUNSUPPORTED),
+])
+def test_fused_swiglu_rejects(lib, kw, code):
+    assert fused(lib, **kw) == code
+    assert lib.mgg_last_error() != b""
 
 
 def test_fp4_kgrouped_unsupported(lib):

@@ -223,3 +223,101 @@ def test_chain_graph_replay_changing_routing():
         torch.cuda.synchronize()
         assert (got == bf16_bits(c.D)).all(), f"replay differs from eager in phase {ph}"
         c.check_stages()
+
+
+# ----------------------------------------------------------------------------- fused
+
+
+FUSED_TYPES = [("fp8", "ue8m0", "block128"), ("fp8", "f32", "block128"),
+               ("fp8", "f32", "channel"), ("fp8_fp4", "ue8m0", "block32")]
+
+
+def fused_vs_separate(p, sfq, z=1.0):
+    """The fused entry point and the two separate steps on the same problem; returns
+    (Qf, SFf, Qs, SFs, valid rows). Outputs start from fill patterns so that rows the
+    fused call must not touch can be checked."""
+    import moe_grouped_gemm_nt_amd as mgg
+    I = p.N // 2
+    H = sentinel_like((p.M, p.N), DEV)
+    mgg.grouped_gemm_contiguous(p.A, p.B, H, p.m_indices, p.SFA, p.SFB, p.sfb_gran, 128)
+    Qs, SFs = mgg.swiglu_quant_fp8_1x128(H, sf_fmt=sfq, sf_zero=z)
+    Qf = torch.full((p.M, I), 0xAB, dtype=torch.uint8, device=DEV)
+    sfd = torch.float32 if sfq == "f32" else torch.uint8
+    SFf = torch.full((I // 128, p.M), 77, dtype=sfd, device=DEV)
+    mgg.grouped_gemm_contiguous_swiglu_quant(p.A, p.B, p.m_indices, p.SFA, p.SFB, Qf, SFf,
+                                             sfq_fmt=sfq, sf_zero=z, sfb_gran=p.sfb_gran)
+    torch.cuda.synchronize()
+    valid = torch.from_numpy(p.meta["m_indices"] >= 0).to(DEV)
+    return Qf, SFf, Qs, SFs, valid
+
+
+def assert_fused_equal(Qf, SFf, Qs, SFs, valid):
+    assert torch.equal(Qf[valid], Qs[valid]), "codes differ from the separate steps"
+    assert torch.equal(SFf[:, valid].view(torch.uint8), SFs[:, valid].view(torch.uint8)), \
+        "scales differ from the separate steps"
+    assert (Qf[~valid] == 0xAB).all(), "rows that are not routed were written"
+    assert (SFf[:, ~valid] == 77).all(), "scales of rows that are not routed were written"
+
+
+@pytest.mark.parametrize("dt,sf,gran", FUSED_TYPES)
+@pytest.mark.parametrize("sfq", ["ue8m0", "f32"])
+def test_fused_swiglu_matches_separate_steps(dt, sf, gran, sfq):
+    """Ragged segments, I = 384 (three output groups, so gate and up blocks are gathered
+    from different places), K = 512: bit-identical to GEMM -> SwiGLU + quantization."""
+    segs = [130, 0, 1, 127, 128, 45]
+    say("fused", dt, sf, gran, sfq, segs)
+    p = synth.make_contiguous(dt, len(segs), 768, 512, segs, seed=50, device=DEV, sf_fmt=sf,
+                              sfb_gran=gran, M_max=1152, std_b=0.05)
+    assert_fused_equal(*fused_vs_separate(p, sfq, z=1e-4))
+
+
+def test_fused_swiglu_full_w13_shape():
+    """The contiguous configuration's w13 (288 experts, I = 256, K = 4096, UE8M0): every
+    routed row bit-identical to the separate steps."""
+    say("fused full w13")
+    p, _ = synth.make_workload("contig_fp8_w13", DEV)
+    assert_fused_equal(*fused_vs_separate(p, "ue8m0"))
+
+
+def test_fused_chain_graph_replay_changing_routing():
+    """Fused w13 + w2 captured in one graph and replayed with new routing values: every
+    replay equals the eager chain and the separate steps, and the oracle chain within the
+    FP8 bar."""
+    import moe_grouped_gemm_nt_amd as mgg
+    G, Hd, I, M = 8, 512, 256, 2048
+    rng = np.random.default_rng(51)
+    draws = [np.minimum(rng.poisson(90, G), 128) for _ in range(2)]
+    draws += [np.zeros(G, int), np.minimum(rng.poisson(120, G), 128)]
+    say("fused chain graph")
+    c = Chain(G, Hd, I, M, draws[0], "ue8m0", seed=51)
+    p = c.p13
+
+    def run():
+        mgg.grouped_gemm_contiguous_swiglu_quant(p.A, p.B, p.m_indices, p.SFA, p.SFB, c.Q, c.SF,
+                                                 sfq_fmt="ue8m0")
+        mgg.grouped_gemm_contiguous(c.Q, c.B2, c.D, p.m_indices, c.SF, c.SFB2, p.sfb_gran, 64)
+
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    fill = sentinel_like((M, Hd), DEV)
+    for ph, segs in enumerate(draws):
+        say("  phase", ph, segs.tolist())
+        c.set_routing(segs)
+        c.D.copy_(fill)
+        g.replay()
+        torch.cuda.synchronize()
+        got = bf16_bits(c.D)
+        c.D.copy_(fill)
+        run()
+        torch.cuda.synchronize()
+        assert (got == bf16_bits(c.D)).all(), f"replay differs from eager in phase {ph}"
+        valid = np.nonzero(p.meta["m_indices"] >= 0)[0]
+        if valid.size:
+            vv, ref = c.oracle_end_to_end()
+            gpu = oracle.decode_bf16(bf16_bits(c.D)[vv])
+            diff = oracle.calc_diff(gpu, oracle.decode_bf16(oracle.round_to_bf16(ref)))
+            say("  end-to-end calc_diff", diff)
+            assert diff < 1e-3
