@@ -1,8 +1,9 @@
 // gemm_engine.h - the gfx950 grouped NT GEMM engine shared by the masked, contiguous
 // and K-grouped entry points.
 //
-// One persistent kernel per call. Each workgroup (4 wave64s; 8 when an accumulation
-// input is read, see below):
+// One persistent kernel per call. Each workgroup (four copy waves, four or eight MFMA
+// waves, and four epilogue waves when an accumulation input is read; see
+// grouped_gemm_kernel.h):
 //   1. reads the device-side routing (masked counts, contiguous row indices, K-grouped
 //      token counts) into LDS and builds the tile prefix there, so nothing about the
 //      expert distribution is baked into the launch (a captured hipGraph replays

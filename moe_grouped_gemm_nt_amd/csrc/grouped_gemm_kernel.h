@@ -4,7 +4,8 @@
 // granularity, accumulation) combination the host dispatcher can pick.
 //
 // Pipeline. A workgroup walks a flat sequence of work items (tile, 128-byte K slice)
-// with three groups of four waves (two without an accumulation input):
+// with four copy waves, four or eight MFMA waves and, with an accumulation input, four
+// epilogue waves:
 //   - copy waves run the issue cursor: they start the direct global -> LDS copies of
 //     item i + S - 1 into ring stage (i + S - 1) % S. Each copy wave issues the same
 //     number of copy instructions for every item (out-of-range lanes and idle items
