@@ -49,15 +49,24 @@ def kernel_name(workload: str) -> str:
     return QUANT_KERNEL_NAME if workload in QUANT_WORKLOADS else KERNEL_NAME
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and blank lines (edits to comments leave the kernel,
+    and so its counter readings, unchanged)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_digest(kernel: str = KERNEL_NAME) -> str:
-    """SHA-256 over the sources a kernel is built from (names and bytes), so that HBM
-    counter readings taken on one version of the kernel are never reported for another."""
+    """SHA-256 over the code (comments stripped) of the sources a kernel is built from, so
+    that HBM counter readings taken on one version of the kernel are never reported for
+    another."""
     import hashlib
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
         h.update(name.encode())
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 
