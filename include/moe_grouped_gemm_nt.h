@@ -66,7 +66,7 @@ extern "C" {
 typedef enum {
   MGG_OK = 0,
   MGG_EINVAL = 1,       /* a host argument is invalid; nothing enqueued */
-  MGG_EUNSUPPORTED = 2, /* valid but outside what this build implements; nothing enqueued */
+  MGG_EUNSUPPORTED = 2, /* valid but outside what the library implements; nothing enqueued */
   MGG_EHIP = 3          /* the HIP runtime reported an error at launch */
 } mgg_status;
 

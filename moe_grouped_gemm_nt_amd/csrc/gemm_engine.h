@@ -64,6 +64,9 @@ constexpr int kContigBlock = 128; // rows per contiguous-layout alignment block
 constexpr int kMaxExperts = 4096;  // the expert index shares an int with the block index
 constexpr int kMaxContigBlocks = 4096;
 constexpr int kLdsBytes = 160 * 1024;  // per workgroup on gfx950
+// Flag on a K-grouped expert's scheduler entry (its token prefix, at most 2^28 + 1):
+// the expert is outside the routing contract and is skipped.
+constexpr int kKUnusable = 1 << 30;
 
 struct Params {
   const uint8_t* A;
@@ -171,6 +174,44 @@ __device__ void block_inclusive_max(int* buf, int n, int* s_tmp) {
     buf[i] = run;
   }
   __syncthreads();
+}
+
+// Exclusive scan like block_exclusive_scan, for values in [0, cap] with every partial
+// sum saturating at cap (min(a + b, cap) is associative on non-negative values, so the
+// result is the exact prefix clamped to cap); 2 * cap must fit an int. Returns the
+// saturated total.
+template <int NT>
+__device__ int block_exclusive_scan_sat(int* buf, int n, int* s_tmp, int cap) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (n + NT - 1) / NT;
+  const int lo = tid * per;
+  const int hi = min(lo + per, n);
+  int local = 0;
+  for (int i = lo; i < hi; ++i) local = min(local + buf[i], cap);
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl = min(incl + v, cap);
+  }
+  int excl = __shfl_up(incl, 1, 64);  // saturated sums do not subtract: shift instead
+  if (lane == 0) excl = 0;
+  if (lane == 63) s_tmp[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    if (w < wave) before = min(before + s_tmp[w], cap);
+    total = min(total + s_tmp[w], cap);
+  }
+  int run = min(before + excl, cap);
+  for (int i = lo; i < hi; ++i) {
+    const int v = buf[i];
+    buf[i] = run;
+    run = min(run + v, cap);
+  }
+  __syncthreads();
+  return total;
 }
 
 // Exclusive scan of `n` ints held in LDS `buf` (in place), block-wide over NT threads;

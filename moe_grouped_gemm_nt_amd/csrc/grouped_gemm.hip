@@ -79,6 +79,9 @@ void sched_bytes(const Params& p, long* persistent, long* transient) {
     const long nb = cdiv(p.rows, kContigBlock);
     *persistent = nb * 4;
     *transient = (kThreads + 2 * nb) * 4;
+  } else if (VAR == kKGrouped) {
+    *persistent = (p.G + 1L) * 4;         // token prefixes and their total
+    *transient = (kThreads + p.G) * 4L;  // scan scratch, clamped counts
   } else {
     *persistent = (VAR == kPsum ? 3L : 2L) * p.G * 4;
     *transient = kThreads * 4;

@@ -54,9 +54,10 @@ struct TileCtx {
 
 template <class T, int VAR>
 struct Sched {
-  int* s_a;    // masked: tile prefix [G]; K-grouped: p_e [G]
+  int* s_a;    // masked, psum: tile prefix [G]; K-grouped: p_e [G + 1], with
+               // kKUnusable set on experts outside the routing contract
   int* s_b;    // masked, psum: row counts [G]; contiguous: packed (block << 12 | expert)
-               // of each valid block; K-grouped: usable k_e or -1 [G]
+               // of each valid block
   int* s_c;    // psum: first row of each expert's segment [G]
   int total;   // number of tiles
   int ntn;     // n tiles per expert
@@ -205,20 +206,30 @@ __device__ __forceinline__ void sched_init(Sched<T, VAR>& S, const Params& p, in
     __syncthreads();
     S.total = nvalid * SUB * S.ntn;
   } else {
+    // p_e = sum_{j<e} max(k_j, 0) saturated at K + 1: an expert is usable only if its
+    // tokens end at or before K, so the saturation changes no decision, and no routing
+    // value can overflow the prefix or move an operand base outside its tensor. A usable
+    // expert's count is p_{e+1} - p_e (p_G closes the table).
+    // The counts, clamped to [-1, K + 1] (which keeps every decision), wait in s_flag
+    // (transient) so the routing buffer is read once.
     S.mtn = (p.rows + T::BM - 1) / T::BM;
+    const int cap = p.K + 1;  // K <= 2^28
     for (int g = tid; g < p.G; g += NT) {
-      const int k = p.meta_psum ? p.meta[g] - (g > 0 ? p.meta[g - 1] : 0) : p.meta[g];
-      S.s_b[g] = k;
-      S.s_a[g] = k > 0 ? k : 0;
+      const long k = p.meta_psum ? (long)p.meta[g] - (g > 0 ? (long)p.meta[g - 1] : 0L)
+                                 : (long)p.meta[g];
+      const int kc = k < 0 ? -1 : (k > cap ? cap : (int)k);
+      s_flag[g] = kc;
+      S.s_a[g] = kc < 0 ? 0 : kc;
     }
     __syncthreads();
-    block_exclusive_scan<NT>(S.s_a, p.G, s_tmp);
+    const int pg = block_exclusive_scan_sat<NT>(S.s_a, p.G, s_tmp, cap);
+    if (tid == 0) S.s_a[p.G] = pg;
     for (int g = tid; g < p.G; g += NT) {
-      const int k = S.s_b[g];
+      const int k = s_flag[g];
       const int pe = S.s_a[g];
       const bool usable = k >= 0 && (k % p.k_granule) == 0 && (pe % p.k_granule) == 0 &&
-                          (long)pe + k <= (long)p.K;
-      S.s_b[g] = usable ? k : -1;
+                          pe + k <= p.K;
+      if (!usable) S.s_a[g] = pe | kKUnusable;
     }
     __syncthreads();
     S.total = p.G * S.mtn * S.ntn;
@@ -334,14 +345,15 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       const int per = S.mtn * S.ntn;
       const int e = (int)(L / per);
       const int local = (int)(L % per);
-      const int k = S.s_b[e];
-      if (k < 0 || (k == 0 && p.accumulate)) { L += gridDim.x; continue; }  // nothing to write
+      const int se = __builtin_amdgcn_readfirstlane(S.s_a[e]);
+      const int k = (__builtin_amdgcn_readfirstlane(S.s_a[e + 1]) & ~kKUnusable) - se;
+      if ((se & kKUnusable) || (k == 0 && p.accumulate)) { L += gridDim.x; continue; }
       // n-tile fastest: the tiles an XCD runs at once cover whole output rows, so the
       // accumulation input and output stream through long contiguous runs (measured 2 %
       // faster than m-tile fastest on the weight-gradient shape; the operands are small
       // enough to stay in L2 either way)
       const int mt = local / S.ntn, nt = local % S.ntn;
-      const long pe = S.s_a[e];
+      const long pe = se;
       t.valid = 1;
       t.g = e;
       t.m0 = mt * T::BM;
@@ -477,7 +489,7 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
     int* base = reinterpret_cast<int*>(smem + Lay::SCHED_OFF);
     const int n = (VAR == kContig) ? (p.rows + kContigBlock - 1) / kContigBlock : p.G;
     Sd.s_a = base;
-    Sd.s_b = base + (VAR == kContig ? 0 : n);
+    Sd.s_b = base + (VAR == kContig ? 0 : n);  // unused by K-grouped calls
     Sd.s_c = base + 2 * n;
     int* s_tmp = reinterpret_cast<int*>(smem);
     int* s_flag = s_tmp + kThreads;

@@ -378,7 +378,7 @@ def make_kgrouped(dtype: str, ks, M: int, N: int, seed: int, device="cpu",
 #   masked_*_g32_n6144     PR's latency table, row G=32 cap=4096 N=6144 K=7168 expected M 192
 #   masked_*_g6_n4096      PR's latency table, row G=6 cap=4096 N=K=4096 expected M 1024
 # Per-expert valid rows are drawn ~Poisson(expected M), clipped to the capacity (the
-# pages give only the expected value; the distribution is this build's choice).
+# pages give only the expected value; the Poisson shape is an assumption).
 
 WORKLOADS = {
     "masked_bf16_repro": dict(variant="masked", dtype="bf16", G=8, cap=32, N=256, K=256,

@@ -166,8 +166,6 @@ def check_contiguous(p: synth.Problem, D: torch.Tensor, rows=None, cols=None,
     Dh = bf16_bits(D)
     idx = p.meta["m_indices"]
     expert = oracle.contiguous_row_expert(idx, p.G)
-    A = np_codes(p.A)
-    SFA = None if p.SFA is None else np_codes(p.SFA)
     want = expert >= 0
     if rows is not None:
         sel = np.zeros(p.M, bool)
@@ -181,10 +179,13 @@ def check_contiguous(p: synth.Problem, D: torch.Tensor, rows=None, cols=None,
         B = np_codes(p.B[int(g)])[None]
         SFB = None if p.SFB is None else np_codes(p.SFB[int(g)])[None]
         sub_idx = np.zeros(r_idx.size, np.int32)
-        sfa = None if SFA is None else SFA[:, r_idx]
-        ref, _ = oracle.grouped_gemm_contiguous(p.dtype, A[r_idx], B, sub_idx, sfa, SFB,
+        # only the rows under test leave the device (operands may be gigabytes)
+        sel_t = torch.from_numpy(r_idx).to(p.A.device)
+        A_r = np_codes(p.A.index_select(0, sel_t))
+        sfa = None if p.SFA is None else np_codes(p.SFA.index_select(1, sel_t))
+        ref, _ = oracle.grouped_gemm_contiguous(p.dtype, A_r, B, sub_idx, sfa, SFB,
                                                 p.sfb_gran, p.sf_fmt, cols=cc)
-        S, _ = oracle.grouped_gemm_contiguous(p.dtype, abs_codes(A[r_idx], p.dtype),
+        S, _ = oracle.grouped_gemm_contiguous(p.dtype, abs_codes(A_r, p.dtype),
                                               abs_codes(B, p.dtype, True), sub_idx, sfa, SFB,
                                               p.sfb_gran, p.sf_fmt, cols=cc)
         ref, S = ref[:, cc], S[:, cc]

@@ -345,3 +345,41 @@ def test_kgrouped_psum_matches_counts(dtype):
     torch.cuda.synchronize()
     assert torch.equal(D1, D2)
     assert_report(check_kgrouped(p, D2), dtype)
+
+
+@pytest.mark.parametrize("mode", ["counts", "psum"])
+def test_kgrouped_routing_beyond_int32(mode):
+    """Routing values whose token prefix leaves the int32 range (K_total = 512).
+    Counts [-128, 256, 2^31 - 128, 128]: expert 1 owns tokens 0 .. 255, expert 3 would
+    start at token 2^31 + 128 (a 32-bit prefix wraps it to -2^31 + 128, a multiple of 128
+    that passes the bounds test). Cumulative ends [256, 2^31 - 128, -2^31, -2^31 + 256]:
+    expert 0 owns tokens 0 .. 255, expert 2's count is -(2^32 - 128) (+128 in 32-bit
+    arithmetic, which would wrap expert 3's prefix to -2^31). Skipped experts keep D
+    untouched; the usable one matches the oracle, which takes the exact counts."""
+    import dataclasses
+    import moe_grouped_gemm_nt_amd as mgg
+    p = synth.make_kgrouped("fp8", [256, 128, 128], 64, 96, seed=31, std_a=1.0, std_b=1.0,
+                            device=DEV)
+    if mode == "counts":
+        route = [-128, 256, 2 ** 31 - 128, 128]
+        eff, want = route, [False, True, False, False]
+    else:
+        route = [256, 2 ** 31 - 128, -2 ** 31, -2 ** 31 + 256]
+        eff = [route[0]] + [route[e] - route[e - 1] for e in range(1, 4)]
+        want = [True, False, False, False]
+    say("kgrouped routing beyond int32", mode, route)
+    G = len(route)
+    g = torch.Generator(device=DEV).manual_seed(31)
+    C = torch.randn((G, p.M, p.N), device=DEV, generator=g)
+    D = C.clone()
+    mgg.grouped_gemm_kgrouped(p.A, p.B, D, torch.tensor(route, dtype=torch.int32, device=DEV),
+                              p.M, p.N, p.SFA, p.SFB, accumulate=True, psum=(mode == "psum"))
+    torch.cuda.synchronize()
+    q = dataclasses.replace(p, G=G, meta=dict(p.meta, ks=np.asarray(eff, np.int64)))
+    rep = check_kgrouped(q, D, C=C)
+    usable = (~np.isnan(rep["ref"]).all(axis=(1, 2))).tolist()
+    assert usable == want, usable
+    for e in range(G):
+        if not want[e]:
+            assert torch.equal(D[e], C[e]), f"expert {e} must be left untouched"
+    assert_report(rep, "fp8")
