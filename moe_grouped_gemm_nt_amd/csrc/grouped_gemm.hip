@@ -6,10 +6,12 @@
 // buffers itself, so a call captured into a hipGraph stays correct when the routing
 // values change between replays.
 
+#include <map>
 #include <mutex>
 #include <type_traits>
 #include <string>
 #include <unordered_map>
+#include <utility>
 
 #include "grouped_gemm_kernel.h"
 #include "moe_grouped_gemm_nt.h"
@@ -45,12 +47,15 @@ using TileK = Tile<64, 128, 2, 2, 3>;    // K-grouped output tiles
 enum TileId { kTileS = 0, kTileM = 1, kTileL = 2 };
 
 struct DevInfo {
+  int id = 0;
   int cus = 0;
 };
 
 std::mutex g_mu;
 std::unordered_map<int, DevInfo> g_dev;
-std::unordered_map<const void*, int> g_occ;  // kernel -> resident workgroups per CU
+// (device, kernel) -> resident workgroups per CU; the LDS limit attribute is set once per
+// pair, with that device current
+std::map<std::pair<int, const void*>, int> g_occ;
 
 bool dev_info(DevInfo* out) {
   int dev = 0;
@@ -62,6 +67,7 @@ bool dev_info(DevInfo* out) {
     return true;
   }
   DevInfo d;
+  d.id = dev;
   if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return false;
   g_dev[dev] = d;
@@ -109,7 +115,8 @@ mgg_status launch(const Params& p, long max_tiles, hipStream_t stream) {
   int occ = 1;
   {
     std::lock_guard<std::mutex> lk(g_mu);
-    auto it = g_occ.find((const void*)kern);
+    const std::pair<int, const void*> key(dev.id, (const void*)kern);
+    auto it = g_occ.find(key);
     if (it == g_occ.end()) {
       if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                               kLdsBytes) != hipSuccess)
@@ -120,7 +127,7 @@ mgg_status launch(const Params& p, long max_tiles, hipStream_t stream) {
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, Lay::NT, lds_typ) !=
               hipSuccess || o < 1)
         o = 1;
-      g_occ[(const void*)kern] = o;
+      g_occ[key] = o;
       occ = o;
     } else {
       occ = it->second;
