@@ -549,15 +549,19 @@ def summarize(args):
         fac_w = COPY_BYTES / (copy_w * 1024.0)
         fetch = int(round(ker_f * 1024.0 * fac_f))
         write = int(round(ker_w * 1024.0 * fac_w))
-        cmd = ("timeout -s KILL 120 rocprofv3 --pmc {c} -d {d} -o {o} --output-format csv -- "
-               "python -u bench.py --workload {w} --steps {s} --warmup 2{x}")
+        # counters are collected only for the kernel of interest (--kernel-include-regex), so
+        # the many small kernels that generate the inputs run unprofiled
+        cmd = ("timeout -s KILL 150 rocprofv3 --kernel-include-regex {rx} --pmc {c} -d {d} "
+               "-o w --output-format csv -- python -u bench.py --workload {w} --steps {s} "
+               "--warmup 2{x}")
         lines = [f"# {kn}: HBM traffic, workload {w}", "",
-                 "Commands (repository root, one MI355X), one counter per run:", ""]
-        for c, d, ww, o, s, x in [("FETCH_SIZE", cf, "copy_calibration", "copy", 10, ""),
-                                  ("WRITE_SIZE", cw, "copy_calibration", "copy", 10, ""),
-                                  ("FETCH_SIZE", kf, w, "w", 20, " --no-cpu-baseline"),
-                                  ("WRITE_SIZE", kw, w, "w", 20, " --no-cpu-baseline")]:
-            lines.append("    " + cmd.format(c=c, d=d, o=o, w=ww, s=s, x=x))
+                 "Commands (repository root, one MI355X, `export TMPDIR=/tmp` first), one "
+                 "counter per run:", ""]
+        for c, d, ww, rx, s, x in [("FETCH_SIZE", cf, "copy_calibration", "copy", 10, ""),
+                                   ("WRITE_SIZE", cw, "copy_calibration", "copy", 10, ""),
+                                   ("FETCH_SIZE", kf, w, kn, 20, " --no-cpu-baseline"),
+                                   ("WRITE_SIZE", kw, w, kn, 20, " --no-cpu-baseline")]:
+            lines.append("    " + cmd.format(c=c, d=d, rx=rx, w=ww, s=s, x=x))
         lines += ["", "Calibration: the copy reads and writes exactly "
                   f"{COPY_BYTES} B per launch; its median FETCH_SIZE is {copy_f:.1f} KiB and "
                   f"WRITE_SIZE {copy_w:.1f} KiB, so the counters are scaled by "
