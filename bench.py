@@ -11,8 +11,9 @@ does); --workload picks any other named workload.
 Timing: `--warmup` untimed steps, then exactly `--steps` steps captured into one
 hipGraph and replayed once between HIP events recorded on the launch stream, bracketed
 by device synchronization (the pages' method also times graph-captured calls). Outputs
-rotate over enough buffers that their footprint exceeds the 256 MB Infinity Cache, so
-each step streams its output from HBM.
+rotate over enough buffers that their footprint exceeds the 256 MB Infinity Cache, and so
+do copies of the inputs (the bytes each step reads, times the copies, exceed four times
+the cache), so each step reads its operands from HBM and writes its output there.
 
 Prints one JSON line with the metric, the roofline of the kernel and the CPU oracle's
 throughput on a bounded sample of the same workload.
@@ -100,6 +101,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--rotate-inputs", type=int, default=0,
+                    help="input copies rotated over the steps (default: enough that the bytes "
+                         "read per cycle exceed four times the Infinity Cache; 1 keeps the "
+                         "inputs warm)")
     ap.add_argument("--rotate", type=int, default=0,
                     help="output buffers to rotate over (0: enough to exceed the MALL)")
     ap.add_argument("--summarize-trace", metavar="DIR",
@@ -111,6 +116,19 @@ def parse():
                          "output of four `rocprofv3 --pmc` runs: FETCH_SIZE and WRITE_SIZE of "
                          "--workload copy_calibration, then of the workload")
     return ap.parse_args()
+
+
+def algorithmic_output_bytes(p, opt) -> int:
+    """The output part of algorithmic_bytes: valid output rows written once (and read once
+    more when accumulating)."""
+    import numpy as np
+    if p.variant == "kgrouped":
+        return p.G * p.M * p.N * 4 * (2 if opt.get("accumulate", True) else 1)
+    if p.variant == "masked":
+        rows = int(np.clip(p.meta["counts"], 0, p.cap).sum())
+    else:
+        rows = int((p.meta["m_indices"] >= 0).sum())
+    return rows * p.N * 2
 
 
 def algorithmic_bytes(p, opt) -> int:
@@ -189,16 +207,32 @@ def main():
     nrot = args.rotate if args.rotate > 0 else max(1, min(8, -(-2 * MALL_BYTES // out_bytes)))
     outs = [torch.zeros(out_shape, dtype=out_dtype, device=dev) for _ in range(nrot)]
 
+    # Input copies (same values, other addresses), rotated so that the operand and scale
+    # bytes the steps read over one cycle exceed four times the Infinity Cache: each step
+    # reads its inputs from HBM, as one layer of a model does between the other layers'
+    # calls, instead of from the cache the previous identical step filled (with a cycle
+    # only a little larger than the cache, a policy that keeps the oldest lines would still
+    # serve part of every step from it).
+    in_read = max(1, abytes - algorithmic_output_bytes(p, opt))
+    tensors = [t for t in (p.A, p.B, p.SFA, p.SFB) if t is not None]
+    in_alloc = sum(t.numel() * t.element_size() for t in tensors)
+    nin = args.rotate_inputs if args.rotate_inputs > 0 else -(-4 * MALL_BYTES // in_read)
+    nin = max(1, min(nin, (8 << 30) // max(1, in_alloc)))
+    ins = [(p.A, p.B, p.SFA, p.SFB)]
+    for _ in range(nin - 1):
+        ins.append(tuple(None if t is None else t.clone() for t in (p.A, p.B, p.SFA, p.SFB)))
+
     def step(i):
         D = outs[i % nrot]
+        A, B, SFA, SFB = ins[i % nin]
         if p.variant == "kgrouped":
-            mgg.grouped_gemm_kgrouped(p.A, p.B, D, p.ks, p.M, p.N, p.SFA, p.SFB,
+            mgg.grouped_gemm_kgrouped(A, B, D, p.ks, p.M, p.N, SFA, SFB,
                                       opt.get("accumulate", True))
         elif p.variant == "masked":
-            mgg.grouped_gemm_masked(p.A, p.B, D, p.counts, p.SFA, p.SFB, p.sfb_gran,
+            mgg.grouped_gemm_masked(A, B, D, p.counts, SFA, SFB, p.sfb_gran,
                                     opt["expected_m"])
         else:
-            mgg.grouped_gemm_contiguous(p.A, p.B, D, p.m_indices, p.SFA, p.SFB, p.sfb_gran,
+            mgg.grouped_gemm_contiguous(A, B, D, p.m_indices, SFA, SFB, p.sfb_gran,
                                         opt["expected_m"])
 
     stream = torch.cuda.Stream(dev)
@@ -250,7 +284,8 @@ def main():
 
     cfg = {"workload": args.workload, "variant": p.variant, "dtype": p.dtype, "G": p.G,
            "N": p.N, "K": p.K, "valid_gflop": round(flops / 1e9, 4),
-           "rotating_output_buffers": nrot, "timing": "one hipGraph of `steps` calls"}
+           "rotating_output_buffers": nrot, "rotating_input_copies": nin,
+           "timing": "one hipGraph of `steps` calls"}
     if p.variant == "kgrouped":
         cfg.update(M=p.M, ks=[int(k) for k in p.meta["ks"]],
                    accumulate=bool(opt.get("accumulate", True)), scales="f32 per channel 1x128")
