@@ -118,6 +118,14 @@ def parse():
     return ap.parse_args()
 
 
+def rotated_input_copies(in_read: int, in_alloc: int, requested: int = 0) -> int:
+    """Input copies to rotate over the timed steps: `requested` when positive, else enough
+    that one cycle reads more than four times the Infinity Cache (in_read bytes per step);
+    never more than 8 GiB of copies (in_alloc bytes each) and at least one."""
+    n = requested if requested > 0 else -(-4 * MALL_BYTES // max(1, in_read))
+    return max(1, min(n, (8 << 30) // max(1, in_alloc)))
+
+
 def algorithmic_output_bytes(p, opt) -> int:
     """The output part of algorithmic_bytes: valid output rows written once (and read once
     more when accumulating)."""
@@ -213,11 +221,10 @@ def main():
     # calls, instead of from the cache the previous identical step filled (with a cycle
     # only a little larger than the cache, a policy that keeps the oldest lines would still
     # serve part of every step from it).
-    in_read = max(1, abytes - algorithmic_output_bytes(p, opt))
+    in_read = abytes - algorithmic_output_bytes(p, opt)
     tensors = [t for t in (p.A, p.B, p.SFA, p.SFB) if t is not None]
     in_alloc = sum(t.numel() * t.element_size() for t in tensors)
-    nin = args.rotate_inputs if args.rotate_inputs > 0 else -(-4 * MALL_BYTES // in_read)
-    nin = max(1, min(nin, (8 << 30) // max(1, in_alloc)))
+    nin = rotated_input_copies(in_read, in_alloc, args.rotate_inputs)
     ins = [(p.A, p.B, p.SFA, p.SFB)]
     for _ in range(nin - 1):
         ins.append(tuple(None if t is None else t.clone() for t in (p.A, p.B, p.SFA, p.SFB)))

@@ -1,0 +1,93 @@
+"""CPU tests of the benchmark's byte accounting: the algorithmic bytes behind the roofline
+and the split into input and output bytes that sizes the rotated input copies. Each
+expected value is recomputed here from the problem's shapes and routing, element by
+element, independently of bench.py's formulas."""
+
+import numpy as np
+import pytest
+
+import bench
+from moe_grouped_gemm_nt_amd import synth
+
+
+def _expected(p, accumulate=True):
+    """(input bytes, output bytes) a perfect kernel moves: every operand element feeding a
+    valid output once, every scale once, valid outputs written once (+ read once when
+    accumulating)."""
+    esz = 2 if p.dtype == "bf16" else 1
+    wsz = 0.5 if p.dtype == "fp8_fp4" else esz
+    sf = 4 if p.sf_fmt == "f32" else 1
+    if p.variant == "kgrouped":
+        T = int(np.sum(p.meta["ks"]))
+        inp = p.M * T * esz + p.N * T * esz
+        if p.dtype != "bf16":
+            inp += (T // 128) * (p.M + p.N) * sf
+        return inp, p.G * p.M * p.N * 4 * (2 if accumulate else 1)
+    if p.variant == "masked":
+        counts = np.clip(p.meta["counts"], 0, p.cap)
+        experts_used = [g for g in range(p.G) if counts[g] > 0]
+        rows = int(counts.sum())
+    else:
+        idx = p.meta["m_indices"]
+        experts_used = sorted(set(int(e) for e in idx if e >= 0))
+        rows = int((idx >= 0).sum())
+    kb = p.K // 128
+    inp = 0
+    for _ in range(rows):  # activation row and its scales
+        inp += p.K * esz + (kb * sf if p.dtype != "bf16" else 0)
+    for _ in experts_used:  # each used expert's weights and weight scales, once
+        inp += int(p.N * p.K * wsz)
+        if p.dtype != "bf16":
+            per = {"block128": -(-p.N // 128) * kb, "channel": p.N * kb,
+                   "block32": p.N * kb * 4}[p.sfb_gran]
+            inp += per * sf
+    return inp, rows * p.N * 2
+
+
+CASES = [
+    ("masked", dict(dtype="bf16", G=4, cap=40, N=64, K=256, counts=[0, 40, 7, 100])),
+    ("masked", dict(dtype="fp8", G=3, cap=33, N=136, K=384, counts=[33, 0, 5])),
+    ("masked", dict(dtype="fp8", G=3, cap=33, N=136, K=384, counts=[1, 2, 3],
+                    sf_fmt="ue8m0", sfb_gran="channel")),
+    ("masked", dict(dtype="fp8_fp4", G=2, cap=16, N=128, K=256, counts=[16, 9],
+                    sf_fmt="ue8m0", sfb_gran="block32")),
+    ("contiguous", dict(dtype="fp8", G=4, N=200, K=256, seg_counts=[130, 0, 1, 127],
+                        sf_fmt="ue8m0")),
+    ("contiguous", dict(dtype="bf16", G=3, N=64, K=128, seg_counts=[5, 128, 0])),
+    ("kgrouped", dict(dtype="fp8", ks=[256, 128, 0, 128], M=64, N=96)),
+    ("kgrouped", dict(dtype="bf16", ks=[8, 24], M=32, N=16)),
+]
+
+
+@pytest.mark.parametrize("kind,kw", CASES)
+@pytest.mark.parametrize("accumulate", [True, False])
+def test_algorithmic_bytes_split(kind, kw, accumulate):
+    kw = dict(kw)
+    if kind == "masked":
+        p = synth.make_masked(kw.pop("dtype"), kw.pop("G"), kw.pop("cap"), kw.pop("N"),
+                              kw.pop("K"), kw.pop("counts"), seed=1, **kw)
+    elif kind == "contiguous":
+        p = synth.make_contiguous(kw.pop("dtype"), kw.pop("G"), kw.pop("N"), kw.pop("K"),
+                                  kw.pop("seg_counts"), seed=2, **kw)
+    else:
+        p = synth.make_kgrouped(kw.pop("dtype"), kw.pop("ks"), kw.pop("M"), kw.pop("N"),
+                                seed=3)
+    opt = {"accumulate": accumulate, "expected_m": 0}
+    exp_in, exp_out = _expected(p, accumulate)
+    assert bench.algorithmic_output_bytes(p, opt) == exp_out
+    assert bench.algorithmic_bytes(p, opt) == exp_in + exp_out
+
+
+def test_rotated_input_copies():
+    """Default copies: one cycle reads at least four times the Infinity Cache and one copy
+    fewer would not; the 8 GiB allocation cap and an explicit request take precedence."""
+    mall = bench.MALL_BYTES
+    for in_read in (1, 3_200_000, 102_000_000, 126_000_000, 737_000_000, 1_600_000_000):
+        n = bench.rotated_input_copies(in_read, in_read)
+        assert n * in_read >= 4 * mall
+        assert n == 1 or (n - 1) * in_read < 4 * mall
+    # a 3.2 MB read from a 6 GB allocation (mostly unread capacity rows): capped at one copy
+    assert bench.rotated_input_copies(3_200_000, 6 << 30) == 1
+    assert bench.rotated_input_copies(3_200_000, 1 << 30) == 8
+    assert bench.rotated_input_copies(102_000_000, 377_000_000, requested=1) == 1
+    assert bench.rotated_input_copies(102_000_000, 377_000_000, requested=3) == 3
