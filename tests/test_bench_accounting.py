@@ -1,7 +1,9 @@
-"""CPU tests of the benchmark's byte accounting: the algorithmic bytes behind the roofline
+"""CPU tests of the benchmark's host logic: the algorithmic bytes behind the roofline
 and the split into input and output bytes that sizes the rotated input copies. Each
 expected value is recomputed here from the problem's shapes and routing, element by
-element, independently of bench.py's formulas."""
+element, independently of bench.py's formulas; the refusal of more than one GPU;
+and the rule that HBM counter readings are reported only for the kernel sources they were
+taken on."""
 
 import numpy as np
 import pytest
@@ -91,3 +93,43 @@ def test_rotated_input_copies():
     assert bench.rotated_input_copies(3_200_000, 1 << 30) == 8
     assert bench.rotated_input_copies(102_000_000, 377_000_000, requested=1) == 1
     assert bench.rotated_input_copies(102_000_000, 377_000_000, requested=3) == 3
+
+
+def test_more_than_one_gpu_is_refused():
+    """`--gpus N` above 1 ends with a message and a non-zero status, before any GPU work."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+
+
+def test_code_only_ignores_comments_and_blank_lines():
+    a = "int f(int x) {  // twice\n\n  return 2 * x; /* doubled\n over lines */\n}\n"
+    b = "int f(int x) {\n  return 2 * x;\n}"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(b) != bench._code_only(b.replace("2 *", "3 *"))
+
+
+def _traffic_file(root, workload, digest, fetch, write):
+    (root / "profiles").mkdir(exist_ok=True)
+    (root / "profiles" / f"{workload}_hbm_traffic.md").write_text(
+        f"# counters\n\n- kernel-source-sha256: {digest}\n"
+        f"- fetch_bytes_per_launch: {fetch}\n- write_bytes_per_launch: {write}\n")
+
+
+@pytest.mark.parametrize("workload", ["kgrouped_fp8_wgrad", "quant_fp8_1x128_6144x7168"])
+def test_traffic_only_for_the_current_kernel_sources(tmp_path, monkeypatch, workload):
+    """Counter readings are reported only while the kernel's sources hash to the digest
+    stored with them; a stale or missing reading gives None (JSON null)."""
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic(workload) is None
+    current = bench.kernel_source_digest(bench.kernel_name(workload))
+    _traffic_file(tmp_path, workload, current, 1000, 234)
+    assert bench.measured_traffic(workload) == 1234
+    _traffic_file(tmp_path, workload, "0" * 64, 1000, 234)
+    assert bench.measured_traffic(workload) is None
+    # the two kernels are built from different sources, so their digests differ
+    assert bench.kernel_source_digest(bench.KERNEL_NAME) != \
+        bench.kernel_source_digest(bench.QUANT_KERNEL_NAME)
