@@ -2,18 +2,24 @@
 
 One step = one grouped-GEMM call over one batch of synthetic inputs already resident in
 HBM: the group scheduler, operand and scale staging, MFMA main loop, FP8 scale promotion
-and the row-masked epilogue all run inside it. The default workload is the K-grouped
-FP8 weight-gradient GEMM of the DeepGEMM issue "Non-deterministic numerical problem of
-k_grouped_fp8_gemm_nt_contiguous" (ks [256, 128, 128, 256], 2048 x 2048 channels,
-per-channel 1x128 FP32 scales, accumulating into an FP32 output as that issue's call
-does); --workload picks any other named workload.
+and the row-masked epilogue all run inside it. The default workload is the largest
+masked configuration of the performance table in the DeepGEMM PR "Fix cross-expert
+output overwrites in SM90 masked GEMM": 32 experts of capacity 4096, N = 6144, K = 7168,
+valid rows ~ Poisson(192) per expert, FP8 E4M3 with 1x128 activation and 128x128 weight
+float32 scales, bf16 output. --workload picks any other named workload, among them
+`contig_fp8_w13_redraw` / `contig_fp8_w2_redraw`: the 288-expert contiguous GEMMs of the
+DeepGEMM issue "SM120 m_grouped_fp8 contiguous kernel: illegal memory access at CUDA graph
+replay" with the routing redrawn for every captured call (each call reads its own
+pre-uploaded expert-index draw).
 
-Timing: `--warmup` untimed steps, then exactly `--steps` steps captured into one
-hipGraph and replayed once between HIP events recorded on the launch stream, bracketed
-by device synchronization (the pages' method also times graph-captured calls). Outputs
-rotate over enough buffers that their footprint exceeds the 256 MB Infinity Cache, and so
-do copies of the inputs (the bytes each step reads, times the copies, exceed four times
-the cache), so each step reads its operands from HBM and writes its output there.
+Timing: `--warmup` untimed steps, then exactly `--steps` steps captured into one hipGraph;
+the graph is replayed `--samples` times (default 7), each replay between HIP events
+recorded on the launch stream and bracketed by device synchronization, and the median
+replay gives the time per step (the pages' method: the median of 7 event-timed samples
+of graph-captured calls). Outputs rotate over enough buffers that their footprint exceeds
+the 256 MB Infinity Cache, and so do copies of the inputs (the bytes each step reads,
+times the copies, exceed four times the cache), so each step reads its operands from HBM
+and writes its output there.
 
 Prints one JSON line with the metric, the roofline of the kernel and the CPU oracle's
 throughput on a bounded sample of the same workload.
@@ -97,7 +103,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="kgrouped_fp8_wgrad")
+    ap.add_argument("--samples", type=int, default=7,
+                    help="replays of the captured graph of `steps` calls; the median is reported")
+    ap.add_argument("--workload", default="masked_fp8_g32_n6144")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
@@ -200,9 +208,30 @@ def main():
         chain_bench(dev, args)
         return
     mgg.load_library()
-    p, opt = synth.make_workload(args.workload, dev)
-    flops = p.valid_flops()
-    abytes = algorithmic_bytes(p, opt)
+    redraw = args.workload in REDRAW_WORKLOADS
+    base = REDRAW_WORKLOADS[args.workload] if redraw else args.workload
+    p, opt = synth.make_workload(base, dev)
+    routes = None
+    if redraw:
+        # one routing draw per captured call (at most REDRAW_MAX distinct draws, cycled),
+        # uploaded before capture; the counters of each call follow its own draw
+        w = synth.WORKLOADS[base]
+        nr = max(1, min(args.steps, REDRAW_MAX))
+        segs = [synth.contiguous_draw(p.G, w["lam"], w["seed"] + 1000 + r, w["rows_per_expert_max"])
+                for r in range(nr)]
+        idx = [synth.contiguous_indices(sg, synth.GROUP, p.M)[0] for sg in segs]
+        routes = [torch.from_numpy(x).to(dev) for x in idx]
+        per_call_flops = [2.0 * int((x >= 0).sum()) * p.N * p.K for x in idx]
+        per_call_bytes = []
+        for x in idx:
+            p.meta["m_indices"] = x
+            per_call_bytes.append(algorithmic_bytes(p, opt))
+        p.meta["m_indices"] = idx[0]
+        flops = float(np.mean([per_call_flops[i % nr] for i in range(args.steps)]))
+        abytes = int(np.mean([per_call_bytes[i % nr] for i in range(args.steps)]))
+    else:
+        flops = p.valid_flops()
+        abytes = algorithmic_bytes(p, opt)
 
     # Output buffers, rotated so their footprint exceeds the Infinity Cache.
     if p.variant == "kgrouped":
@@ -239,7 +268,8 @@ def main():
             mgg.grouped_gemm_masked(A, B, D, p.counts, SFA, SFB, p.sfb_gran,
                                     opt["expected_m"])
         else:
-            mgg.grouped_gemm_contiguous(A, B, D, p.m_indices, SFA, SFB, p.sfb_gran,
+            route = p.m_indices if routes is None else routes[i % len(routes)]
+            mgg.grouped_gemm_contiguous(A, B, D, route, SFA, SFB, p.sfb_gran,
                                         opt["expected_m"])
 
     stream = torch.cuda.Stream(dev)
@@ -250,26 +280,13 @@ def main():
     torch.cuda.synchronize(dev)
     print(f"[bench] {args.workload}: warmup {args.warmup} done; capturing {args.steps} steps",
           file=sys.stderr, flush=True)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        for i in range(args.steps):
-            step(i)
-    torch.cuda.synchronize(dev)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize(dev)
-    wall0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        t0.record(stream)
-        graph.replay()
-        t1.record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - wall0
-    ms_total = t0.elapsed_time(t1)
+    samples, wall = _timed_graph_samples(dev, stream, args.steps, step, args.samples)
+    ms_total = float(np.median(samples))
     ms_step = ms_total / args.steps
     tflops = flops / (ms_step * 1e-3) / 1e12
-    print(f"[bench] timed {args.steps} steps: {ms_total:.3f} ms on the stream, "
-          f"{wall * 1e3:.3f} ms wall", file=sys.stderr, flush=True)
+    print(f"[bench] {args.samples} replays of {args.steps} steps: median {ms_total:.3f} ms on the "
+          f"stream (min {min(samples):.3f}, max {max(samples):.3f}); {wall * 1e3:.3f} ms wall "
+          "for all replays", file=sys.stderr, flush=True)
 
     ai = flops / abytes
     ridge = MFMA_PEAK_TFLOPS[p.dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -284,23 +301,31 @@ def main():
     roof["traffic"] = measured_traffic(args.workload)
     roof["algorithmic_bytes_per_launch"] = abytes
     roof["avg_launch_us"] = round(ms_step * 1e3, 3)
+    if roof["bound"] == "hbm":
+        roof["mfma_frac"] = round(tflops / MFMA_PEAK_TFLOPS[p.dtype], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(p, opt, flops, args.cpu_seconds)
+        cpu = cpu_baseline(p, opt, p.valid_flops(), args.cpu_seconds)
 
     cfg = {"workload": args.workload, "variant": p.variant, "dtype": p.dtype, "G": p.G,
            "N": p.N, "K": p.K, "valid_gflop": round(flops / 1e9, 4),
            "rotating_output_buffers": nrot, "rotating_input_copies": nin,
-           "timing": "one hipGraph of `steps` calls"}
+           "timing": f"median of {args.samples} replays of one hipGraph of `steps` calls"}
     if p.variant == "kgrouped":
         cfg.update(M=p.M, ks=[int(k) for k in p.meta["ks"]],
                    accumulate=bool(opt.get("accumulate", True)), scales="f32 per channel 1x128")
     elif p.variant == "masked":
         cfg.update(cap=p.cap, expected_m=opt["expected_m"],
-                   valid_rows=int(np.clip(p.meta["counts"], 0, p.cap).sum()))
+                   valid_rows=int(np.clip(p.meta["counts"], 0, p.cap).sum()),
+                   scales=f"{p.sf_fmt} 1x128 act / {p.sfb_gran} weight" if p.dtype != "bf16" else None)
     else:
-        cfg.update(M=p.M, expected_m=opt["expected_m"], valid_rows=int(p.meta["valid_rows"]))
+        cfg.update(M=p.M, expected_m=opt["expected_m"], valid_rows=int(p.meta["valid_rows"]),
+                   scales=f"{p.sf_fmt} 1x128 act / {p.sfb_gran} weight")
+        if redraw:
+            cfg.update(routing_draws=len(routes),
+                       valid_rows=int(round(flops / (2.0 * p.N * p.K))),
+                       routing="Poisson(113) rows per expert redrawn for every captured call")
     line = {
         "metric": "grouped FP8/BF16 GEMM TFLOPS (valid rows) + % of gfx950 MFMA peak",
         "value": round(tflops, 2),
@@ -322,6 +347,12 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+# the 288-expert contiguous GEMMs with a new routing draw per captured call
+REDRAW_WORKLOADS = {"contig_fp8_w13_redraw": "contig_fp8_w13",
+                    "contig_fp8_w2_redraw": "contig_fp8_w2"}
+REDRAW_MAX = 1000  # distinct draws uploaded (295 KB each at 73728 rows)
+
+
 QUANT_WORKLOADS = {
     # bf16 activations -> FP8 E4M3 codes + 1x128 scales: the expected tokens of the
     # 32-expert N=6144 configuration (32 x 192) at its hidden size 7168
@@ -335,9 +366,18 @@ QUANT_WORKLOADS = {
 }
 
 
-def _timed_graph(dev, stream, steps, fn):
-    """`steps` calls of fn(i) captured in one hipGraph and replayed once between events
-    recorded on the launch stream; returns ms per call."""
+def _timed_graph(dev, stream, steps, fn, samples=7):
+    """`steps` calls of fn(i) captured in one hipGraph; the median of `samples` replays,
+    in ms per call."""
+    import numpy as np
+    out, _ = _timed_graph_samples(dev, stream, steps, fn, samples)
+    return float(np.median(out)) / steps
+
+
+def _timed_graph_samples(dev, stream, steps, fn, samples):
+    """`steps` calls of fn(i) captured in one hipGraph, replayed `samples` times, each
+    replay between events recorded on the launch stream with device synchronization
+    before and after; returns (ms per replay for each sample, wall seconds of all)."""
     import torch
     torch.cuda.synchronize(dev)
     graph = torch.cuda.CUDAGraph()
@@ -345,13 +385,18 @@ def _timed_graph(dev, stream, steps, fn):
         for i in range(steps):
             fn(i)
     torch.cuda.synchronize(dev)
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        t0.record(stream)
-        graph.replay()
-        t1.record(stream)
-    torch.cuda.synchronize(dev)
-    return t0.elapsed_time(t1) / steps
+    out = []
+    wall0 = time.perf_counter()
+    for _ in range(max(1, samples)):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        with torch.cuda.stream(stream):
+            t0.record(stream)
+            graph.replay()
+            t1.record(stream)
+        torch.cuda.synchronize(dev)
+        out.append(t0.elapsed_time(t1))
+    return out, time.perf_counter() - wall0
 
 
 def quant_bench(dev, args):
@@ -382,7 +427,7 @@ def quant_bench(dev, args):
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             step(i)
-    ms_step = _timed_graph(dev, stream, args.steps, step)
+    ms_step = _timed_graph(dev, stream, args.steps, step, args.samples)
     gbs = abytes / (ms_step * 1e-3) / 1e9
     cpu = None
     if not args.no_cpu_baseline:
@@ -408,7 +453,7 @@ def quant_bench(dev, args):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16->e4m3", "data": "synthetic",
         "config": {"workload": args.workload, "M": M, ("I" if swiglu else "K"): K,
                    "scales": fmt, "rotating_buffers": nrot,
-                   "timing": "one hipGraph of `steps` calls"},
+                   "timing": f"median of {args.samples} replays of one hipGraph of `steps` calls"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.workload),
@@ -469,7 +514,7 @@ def chain_bench(dev, args):
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
             chain(i)
-    ms = {name: _timed_graph(dev, stream, args.steps, fn)
+    ms = {name: _timed_graph(dev, stream, args.steps, fn, args.samples)
           for name, fn in (("fused_chain", fused), ("chain", chain), ("w13", k13),
                            ("swiglu_quant", kact), ("w2", k2), ("w13_swiglu_fused", k13f))}
     valid = int(p.meta["valid_rows"])
@@ -492,7 +537,8 @@ def chain_bench(dev, args):
                    "intermediate": I, "valid_rows": valid, "expected_m": em,
                    "scales": p.sf_fmt, "per_launch_us": {k: round(v * 1e3, 3)
                                                          for k, v in ms.items()},
-                   "timing": "one hipGraph of `steps` calls per line"},
+                   "timing": f"median of {args.samples} replays of one hipGraph of `steps` "
+                             "calls per line"},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(dt, 1), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(dt / peak, 4), "traffic": None,
                      "avg_launch_us": round(ms[dom] * 1e3, 3)},

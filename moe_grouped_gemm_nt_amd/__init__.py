@@ -159,6 +159,39 @@ def _require(cond: bool, msg: str):
         raise ValueError(msg)
 
 
+def _check_scales(dt: int, SFA, SFB, sfa_shape, sfb_shapes, gran: str):
+    """Scale tensors against the layouts of include/moe_grouped_gemm_nt.h: none for BF16;
+    for FP8 both present, of one storage type (float32, or uint8 UE8M0) and of exactly the
+    shape the layout and weight-scale granularity fix (`sfb_shapes` maps granularity ->
+    shape). The kernels size their reads from the problem shape, not from the tensors, so
+    a scale tensor of another type or shape would be read out of bounds or misread."""
+    import torch
+    if dt == MGG_BF16:
+        _require(SFA is None and SFB is None, "BF16 operands take no scale tensors")
+        return
+    _require(SFA is not None and SFB is not None, "FP8 operands need SFA and SFB")
+    _require(SFA.dtype in (torch.float32, torch.uint8),
+             f"scales must be float32 or uint8 (UE8M0), got {SFA.dtype}")
+    _require(SFB.dtype == SFA.dtype, f"SFA ({SFA.dtype}) and SFB ({SFB.dtype}) must have the "
+                                     "same storage type")
+    if dt == MGG_FP8_FP4:
+        _require(SFA.dtype == torch.uint8, "FP8 x FP4 products take UE8M0 (uint8) scales")
+    _require(gran in sfb_shapes, f"weight-scale granularity {gran!r} does not fit these operands "
+                                 f"(expected one of {sorted(sfb_shapes)})")
+    _require(tuple(SFA.shape) == tuple(sfa_shape),
+             f"SFA must be {list(sfa_shape)}, got {list(SFA.shape)}")
+    want = tuple(sfb_shapes[gran])
+    _require(tuple(SFB.shape) == want,
+             f"SFB ({gran}) must be {list(want)}, got {list(SFB.shape)}")
+
+
+def _m_sfb_shapes(dt: int, G: int, N: int, K: int) -> dict:
+    """Weight-scale shapes of an M-grouped call per granularity."""
+    if dt == MGG_FP8_FP4:
+        return {"block32": (G, K // 128, N, 4)}
+    return {"block128": (G, -(-N // 128), K // 128), "channel": (G, K // 128, N)}
+
+
 def _same_device(*ts):
     devs = {t.device for t in ts if t is not None}
     _require(len(devs) == 1 and next(iter(devs)).type == "cuda",
@@ -176,9 +209,6 @@ def grouped_gemm_masked(A, B, D, masked_m, SFA=None, SFB=None, sfb_gran=None,
     """D[g, m, :] = A[g, m, :] @ B[g].T for m < masked_m[g]; A[G, cap, K], B[G, N, K],
     D bf16 [G, cap, N], masked_m int32 [G] on the device."""
     import torch
-    lib = load_library()
-    _same_device(A, B, D, masked_m, SFA, SFB)
-    _contig(A, B, D, masked_m, SFA, SFB)
     G, cap, K = A.shape
     N = B.shape[1]
     dt, gran = _m_operands(A, B, K)
@@ -186,6 +216,10 @@ def grouped_gemm_masked(A, B, D, masked_m, SFA=None, SFB=None, sfb_gran=None,
     _require(tuple(D.shape) == (G, cap, N) and D.dtype == torch.bfloat16, "D must be bf16 [G, cap, N]")
     _require(masked_m.dtype == torch.int32 and masked_m.numel() == G, "masked_m must be int32 [G]")
     sfb_gran = sfb_gran or gran
+    _check_scales(dt, SFA, SFB, (G, K // 128, cap), _m_sfb_shapes(dt, G, N, K), sfb_gran)
+    lib = load_library()
+    _same_device(A, B, D, masked_m, SFA, SFB)
+    _contig(A, B, D, masked_m, SFA, SFB)
     with torch.cuda.device(A.device):
         _check(lib.grouped_gemm_masked(dt, G, cap, N, K, _ptr(A), _ptr(SFA), _ptr(B), _ptr(SFB),
                                        _sf_fmt(SFA), _GRAN[sfb_gran], _ptr(D), _ptr(masked_m),
@@ -198,15 +232,16 @@ def grouped_gemm_contiguous(A, B, D, m_indices, SFA=None, SFB=None, sfb_gran=Non
     """D[r, :] = A[r, :] @ B[m_indices[r]].T for rows with a valid expert index;
     A[M, K], B[G, N, K], D bf16 [M, N], m_indices int32 [M] on the device."""
     import torch
-    lib = load_library()
-    _same_device(A, B, D, m_indices, SFA, SFB)
-    _contig(A, B, D, m_indices, SFA, SFB)
     M, K = A.shape
     G, N, _ = B.shape
     dt, gran = _m_operands(A, B, K)
     _require(tuple(D.shape) == (M, N) and D.dtype == torch.bfloat16, "D must be bf16 [M, N]")
     _require(m_indices.dtype == torch.int32 and m_indices.numel() == M, "m_indices must be int32 [M]")
     sfb_gran = sfb_gran or gran
+    _check_scales(dt, SFA, SFB, (K // 128, M), _m_sfb_shapes(dt, G, N, K), sfb_gran)
+    lib = load_library()
+    _same_device(A, B, D, m_indices, SFA, SFB)
+    _contig(A, B, D, m_indices, SFA, SFB)
     with torch.cuda.device(A.device):
         _check(lib.grouped_gemm_contiguous(dt, G, M, N, K, _ptr(A), _ptr(SFA), _ptr(B), _ptr(SFB),
                                            _sf_fmt(SFA), _GRAN[sfb_gran], _ptr(D),
@@ -220,15 +255,16 @@ def grouped_gemm_contiguous_psum(A, B, D, psum, SFA=None, SFB=None, sfb_gran=Non
     (ends clamped to [0, M] and made non-decreasing); A[M, K], B[G, N, K], D bf16 [M, N],
     psum int32 [G] on the device."""
     import torch
-    lib = load_library()
-    _same_device(A, B, D, psum, SFA, SFB)
-    _contig(A, B, D, psum, SFA, SFB)
     M, K = A.shape
     G, N, _ = B.shape
     dt, gran = _m_operands(A, B, K)
     _require(tuple(D.shape) == (M, N) and D.dtype == torch.bfloat16, "D must be bf16 [M, N]")
     _require(psum.dtype == torch.int32 and psum.numel() == G, "psum must be int32 [G]")
     sfb_gran = sfb_gran or gran
+    _check_scales(dt, SFA, SFB, (K // 128, M), _m_sfb_shapes(dt, G, N, K), sfb_gran)
+    lib = load_library()
+    _same_device(A, B, D, psum, SFA, SFB)
+    _contig(A, B, D, psum, SFA, SFB)
     with torch.cuda.device(A.device):
         _check(lib.grouped_gemm_contiguous_psum(dt, G, M, N, K, _ptr(A), _ptr(SFA), _ptr(B),
                                                 _ptr(SFB), _sf_fmt(SFA), _GRAN[sfb_gran],
@@ -244,12 +280,15 @@ def grouped_gemm_contiguous_swiglu_quant(A, B, m_indices, SFA, SFB, Q=None, SFQ=
     rows) -> (Q uint8 [M, I] E4M3 codes, SFQ [I/128, M] float32 or uint8 UE8M0); Q and SFQ
     are allocated when not given; rows that are not routed keep their contents."""
     import torch
-    lib = load_library()
     M, K = A.shape
     G, N2, _ = B.shape
     dt, gran = _m_operands(A, B, K)
     _require(N2 % 2 == 0, "B must hold 2I rows")
     I = N2 // 2
+    sfb_gran = sfb_gran or gran
+    _require(dt != MGG_BF16, "the fused SwiGLU epilogue takes FP8 activations")
+    _check_scales(dt, SFA, SFB, (K // 128, M), _m_sfb_shapes(dt, G, N2, K), sfb_gran)
+    lib = load_library()
     if Q is None:
         Q = torch.empty((M, I), dtype=torch.uint8, device=A.device)
     if SFQ is None:
@@ -264,7 +303,6 @@ def grouped_gemm_contiguous_swiglu_quant(A, B, m_indices, SFA, SFB, Q=None, SFQ=
     _require((SFQ.dtype == torch.float32) == (fmt == MGG_SF_F32), "SFQ dtype must match sfq_fmt")
     _require(m_indices.dtype == torch.int32 and m_indices.numel() == M,
              "m_indices must be int32 [M]")
-    sfb_gran = sfb_gran or gran
     with torch.cuda.device(A.device):
         _check(lib.grouped_gemm_contiguous_swiglu_quant(
             dt, G, M, I, K, _ptr(A), _ptr(SFA), _ptr(B), _ptr(SFB), _sf_fmt(SFA),
@@ -279,9 +317,6 @@ def grouped_gemm_kgrouped(A, B, D, ks, M, N, SFA=None, SFB=None, accumulate=True
     (expert blocks [M][k_e] / [N][k_e]), D fp32 [G, M, N], ks int32 [G] on the device.
     With psum=True, ks holds cumulative token ends (k_e = ks[e] - ks[e-1])."""
     import torch
-    lib = load_library()
-    _same_device(A, B, D, ks, SFA, SFB)
-    _contig(A, B, D, ks, SFA, SFB)
     G = ks.numel()
     _require(A.numel() % M == 0 and B.numel() % N == 0, "packed buffers must hold whole channels")
     K_total = A.numel() // M
@@ -290,6 +325,11 @@ def grouped_gemm_kgrouped(A, B, D, ks, M, N, SFA=None, SFB=None, accumulate=True
     _require(ks.dtype == torch.int32, "ks must be int32")
     dt = _elem_dtype(A)
     _require(_elem_dtype(B) == dt, "A and B must have the same element type")
+    _check_scales(dt, SFA, SFB, (K_total // 128, M), {"channel": (K_total // 128, N)},
+                  "channel")
+    lib = load_library()
+    _same_device(A, B, D, ks, SFA, SFB)
+    _contig(A, B, D, ks, SFA, SFB)
     with torch.cuda.device(A.device):
         fn = lib.grouped_gemm_kgrouped_psum if psum else lib.grouped_gemm_kgrouped
         _check(fn(dt, G, M, N, K_total, _ptr(A), _ptr(SFA), _ptr(B), _ptr(SFB), _sf_fmt(SFA),

@@ -67,19 +67,22 @@ def poisson_counts(G: int, lam: float, cap: int, seed: int) -> np.ndarray:
 
 
 def _scale_from_amax(amax: torch.Tensor, sf_fmt: str, zero_sf: float = 1.0):
-    """amax (float32) -> (scale as float32 values, scale in storage format)."""
+    """Group maxima (float32) -> (the scale each group's codes stand for, as float32; the
+    scale in its storage format). The ratio amax / 448 is the float32 scale; a group with
+    nothing in it (ratio 0) stands for `zero_sf` instead. F32 storage keeps that value,
+    never below 1e-30; UE8M0 storage keeps the exponent of the smallest power of two that
+    is not below it (frexp writes r = f * 2^e with f in [0.5, 1), so that power is 2^e, or
+    2^(e-1) when r is itself a power of two)."""
+    ratio = amax / FP8_MAX
+    ratio = ratio.masked_fill(ratio == 0, zero_sf)
     if sf_fmt == "f32":
-        sf = amax / FP8_MAX
-        sf = torch.where(sf == 0, torch.full_like(sf, zero_sf), sf).clamp_min(1e-30)
-        return sf, sf.contiguous()
+        scale = torch.clamp(ratio, min=1e-30)
+        return scale, scale.contiguous()
     if sf_fmt == "ue8m0":
-        ratio = amax / FP8_MAX
-        mant, exp = torch.frexp(ratio)  # ratio = mant * 2^exp, 0.5 <= mant < 1
-        e = torch.where(mant == 0.5, exp - 1, exp)  # ceil(log2(ratio))
-        e = torch.where(ratio == 0, torch.zeros_like(e), e)
-        code = (e + 127).clamp(0, 254)
-        sf = torch.ldexp(torch.ones_like(ratio), code - 127)
-        return sf, code.to(torch.uint8).contiguous()
+        frac, e = torch.frexp(ratio)
+        e = e - (frac == 0.5).to(e.dtype)
+        code = torch.clamp(e + 127, 0, 254)
+        return torch.ldexp(torch.ones_like(ratio), code - 127), code.to(torch.uint8).contiguous()
     raise ValueError(f"unknown scale format {sf_fmt!r}")
 
 
@@ -87,17 +90,18 @@ def _to_e4m3(x: torch.Tensor) -> torch.Tensor:
     return x.clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
 
 
-def quant_rows_1x128(x: torch.Tensor, sf_fmt: str = "f32"):
+def quant_rows_1x128(x: torch.Tensor, sf_fmt: str = "f32", zero_sf: float = 1.0):
     """Activation rows x[R, K] -> (codes uint8 [R, K], scales [K/128, R]).
 
     One scale per row per 128-element K group; the scale tensor is stored with rows
-    contiguous inside each K group. K must be a multiple of 128.
+    contiguous inside each K group. K must be a multiple of 128. An all-zero group
+    takes `zero_sf`.
     """
     R, K = x.shape
     assert K % GROUP == 0, "FP8 activations need K % 128 == 0"
-    xv = x.float().view(R, K // GROUP, GROUP)
+    xv = x.float().reshape(R, K // GROUP, GROUP)
     amax = xv.abs().amax(dim=2)  # [R, K/128]
-    sf, sf_store = _scale_from_amax(amax, sf_fmt)
+    sf, sf_store = _scale_from_amax(amax, sf_fmt, zero_sf)
     codes = _to_e4m3(xv * (1.0 / sf).unsqueeze(2)).view(R, K)
     return codes.contiguous(), sf_store.t().contiguous()
 
@@ -153,29 +157,22 @@ def quant_weight_fp4_block32(w: torch.Tensor):
     return packed, scales
 
 
-def quant_tokens_per_channel(x: torch.Tensor, sf_val: float = 1.0):
-    """The K-grouped repro's cast: x[T, C] (tokens x channels) -> (codes [T, C],
-    scales float32 [T/128, C]); a channel whose 128-token group is all zero gets sf_val."""
-    T, C = x.shape
-    assert T % GROUP == 0
-    xv = x.float().view(T // GROUP, GROUP, C)
-    amax = xv.abs().amax(dim=1)  # [T/128, C]
-    sf = amax / FP8_MAX
-    sf = torch.where(sf == 0, torch.full_like(sf, sf_val), sf).clamp_min(1e-30)
-    codes = _to_e4m3(xv * (1.0 / sf).unsqueeze(1)).view(T, C)
-    return codes.contiguous(), sf.contiguous()
+def quant_tokens_per_channel(x: torch.Tensor, sf_val: float = 1.0, sf_fmt: str = "f32"):
+    """The K-grouped operands' cast: x[T, C] (tokens x channels) -> (codes [T, C], scales
+    [T/128, C]). A channel's group of 128 consecutive tokens is one row group of x^T, so
+    this is the 1x128 cast of the transposed operand; an all-zero group takes sf_val."""
+    codes_ct, sf = quant_rows_1x128(x.t(), sf_fmt, zero_sf=sf_val)
+    return codes_ct.t().contiguous(), sf
 
 
 def pack_kmajor(x: torch.Tensor, ks) -> torch.Tensor:
-    """Tokens-by-channels x[T, C] -> flat packed buffer: expert e's tokens transposed to
-    [C][k_e], experts laid end to end (offset C * sum of earlier k)."""
-    T, C = x.shape
-    out = torch.empty(T * C, dtype=x.dtype, device=x.device)
-    p = 0
-    for k in ks:
-        out[p * C:(p + k) * C] = x[p:p + k].t().reshape(-1)
-        p += k
-    return out
+    """Tokens-by-channels x[T, C] -> the K-grouped packed layout: x split into the experts'
+    token ranges (k_e tokens each, in order), each range stored channel-major [C][k_e],
+    the ranges one after another in a flat buffer."""
+    parts = torch.split(x, [int(k) for k in ks], dim=0)
+    if not parts:
+        return x.new_empty(0)
+    return torch.cat([part.t().reshape(-1) for part in parts])
 
 
 # --------------------------------------------------------------------------- problems
@@ -327,39 +324,40 @@ def make_contiguous_psum(dtype: str, G: int, N: int, K: int, seg_counts, seed: i
 
 def make_kgrouped(dtype: str, ks, M: int, N: int, seed: int, device="cpu",
                   std_a=1e-7, std_b=0.4, sf_val=1.0, zero_channel_k=128,
-                  K_total: int | None = None) -> Problem:
+                  K_total: int | None = None, sf_fmt: str = "f32") -> Problem:
     """K-grouped problem after the repro recipe: grad_y[T, M] ~ N(0,1)*std_a,
-    act[T, N] ~ N(0,1)*std_b, channel 0 of grad_y zeroed inside every expert that has
-    exactly `zero_channel_k` tokens; both cast per channel per 128 tokens and packed
-    k-major. A = packed grad_y (rows = M channels), B = packed act (rows = N channels)."""
+    act[T, N] ~ N(0,1)*std_b, channel 0 of grad_y zeroed on the tokens of every expert
+    that has exactly `zero_channel_k` of them; both cast per channel per 128 tokens (float32
+    or UE8M0 scales) and packed k-major. A = packed grad_y (rows = M channels), B = packed
+    act (rows = N channels). K_total > sum(ks) appends unrouted zero tokens."""
     ks = [int(k) for k in ks]
     T = sum(ks)
     K_total = T if K_total is None else K_total
     gen = _gen(seed, device)
     gy = randn((T, M), 0, device, std_a, gen=gen)
     act = randn((T, N), 0, device, std_b, gen=gen)
-    p = 0
-    for k in ks:
-        if k == zero_channel_k:
-            gy[p:p + k, 0] = 0
-        p += k
+    if T:
+        counts = torch.tensor(ks, device=device)
+        token_in_small_expert = torch.repeat_interleave(counts == zero_channel_k, counts)
+        gy[:, 0] = gy[:, 0].masked_fill(token_in_small_expert, 0)
     pad = K_total - T
     if dtype == "bf16":
         A = pack_kmajor(gy, ks)
         B = pack_kmajor(act, ks)
         SFA = SFB = None
     else:
-        qa, SFA = quant_tokens_per_channel(gy, sf_val)
-        qb, SFB = quant_tokens_per_channel(act, sf_val)
+        qa, SFA = quant_tokens_per_channel(gy, sf_val, sf_fmt)
+        qb, SFB = quant_tokens_per_channel(act, sf_val, sf_fmt)
         A = pack_kmajor(qa, ks)
         B = pack_kmajor(qb, ks)
         if pad:
-            SFA = torch.cat([SFA, torch.ones((pad // GROUP, M), device=device)])
-            SFB = torch.cat([SFB, torch.ones((pad // GROUP, N), device=device)])
+            unit = torch.ones(()) if sf_fmt == "f32" else torch.tensor(127, dtype=torch.uint8)
+            SFA = torch.cat([SFA, unit.to(device).expand(pad // GROUP, M).to(SFA.dtype)])
+            SFB = torch.cat([SFB, unit.to(device).expand(pad // GROUP, N).to(SFB.dtype)])
     if pad:
         A = torch.cat([A, torch.zeros(pad * M, dtype=A.dtype, device=device)])
         B = torch.cat([B, torch.zeros(pad * N, dtype=B.dtype, device=device)])
-    return Problem("kgrouped", dtype, len(ks), N, K_total, A, B, SFA, SFB, "f32",
+    return Problem("kgrouped", dtype, len(ks), N, K_total, A, B, SFA, SFB, sf_fmt,
                    "channel", M=M, K_total=K_total,
                    ks=torch.tensor(ks, dtype=torch.int32, device=device),
                    meta={"ks": np.asarray(ks, np.int64), "seed": seed, "sf_val": sf_val,

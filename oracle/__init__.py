@@ -20,7 +20,13 @@ Parity status of each function (what pins it lives in tests/test_oracle_*.py):
       power-of-two cases, closed-form groups, round-trip error bound)
   exp_f32, silu_f32, swiglu_values, swiglu_quant_rows_1x128   pinned (float64 exp and
       torch's silu within a few ulps, special values, exact cases where silu(x) = x,
-      equality with the plain quantization of exactly representable products)
+      equality with the plain quantization of exactly representable products); these
+      mirror the kernel's fixed e^y evaluation so codes can be compared bit for bit
+  silu_exact, swiglu_values_exact,
+  swiglu_quant_rows_1x128_exact                               pinned (torch's float64
+      silu, closed-form values, the saturated-gate identity, and agreement with the
+      fixed evaluation up to rounding-boundary flips); the plain definition (float64 exp)
+      that the GPU codes are also compared against
   decode_e2m1, unpack_fp4, the "fp8_fp4" dtype of the M-grouped products   pinned
       (the format's value table, literal nibble cases, exact-rational brute force over
       raw bytes, one-hot weights, equality with the FP8 channel-scale product when the
@@ -45,9 +51,12 @@ from .quantize import (  # noqa: F401
 )
 from .swiglu import (  # noqa: F401
     exp_f32,
+    silu_exact,
     silu_f32,
     swiglu_quant_rows_1x128,
+    swiglu_quant_rows_1x128_exact,
     swiglu_values,
+    swiglu_values_exact,
 )
 from .grouped_gemm import (  # noqa: F401
     MX_BLOCK,

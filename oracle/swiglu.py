@@ -83,3 +83,38 @@ def swiglu_values(h_codes) -> np.ndarray:
 def swiglu_quant_rows_1x128(h_codes, sf_fmt: str = "f32", sf_zero: float = 1.0):
     """bf16 H[M, 2I] -> (Q[M, I] E4M3 codes, SF[I/128, M]) of silu(gate) * up."""
     return quantize_values_1x128(swiglu_values(h_codes), sf_fmt, sf_zero)
+
+
+# --------------------------------------------------------------------------- plain definition
+#
+# The same step from the plain definition, independent of the fixed e^y evaluation above:
+# silu(g) = g / (1 + e^-g) and h = silu(gate) * up evaluated in float64 with the library's
+# exp, then rounded once to float32 (the type the reading fixes for h), then the 1x128
+# cast. The codes of the fixed evaluation can differ from these only where the two h values
+# (relative difference below the fixed evaluation's error, 1e-5, plus a few float32
+# roundings) fall on opposite sides of an E4M3 rounding boundary, or move a group's scale
+# by as much.
+
+
+def silu_exact(x) -> np.ndarray:
+    """x / (1 + e^-x) in float64 (e^-x overflowing to inf gives -0 for very negative x)."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def swiglu_values_exact(h_codes) -> np.ndarray:
+    """bf16 w13 output H[M, 2I] (raw codes) -> float64 h[M, I] = silu(gate) * up."""
+    h = decode_bf16(np.asarray(h_codes)).astype(np.float64)
+    I2 = h.shape[1]
+    if I2 % 2:
+        raise ValueError("the w13 output has an even number of columns")
+    return silu_exact(h[:, : I2 // 2]) * h[:, I2 // 2:]
+
+
+def swiglu_quant_rows_1x128_exact(h_codes, sf_fmt: str = "f32", sf_zero: float = 1.0):
+    """bf16 H[M, 2I] -> (Q[M, I], SF[I/128, M], h[M, I] float32): the 1x128 cast of the
+    plain-definition values, each rounded once to float32."""
+    h32 = swiglu_values_exact(h_codes).astype(np.float32)
+    q, sf = quantize_values_1x128(h32, sf_fmt, sf_zero)
+    return q, sf, h32

@@ -252,25 +252,26 @@ def test_kgrouped_bf16_and_edge_ks():
     assert (D2[0] == 0).all()
 
 
-def test_kgrouped_ue8m0_scales():
-    ks = [128, 384]
-    say("kgrouped ue8m0")
-    p = synth.make_kgrouped("fp8", ks, 128, 128, seed=9, std_a=1.0, std_b=1.0, device=DEV)
-    # re-express the float scales as powers of two with codes re-quantized accordingly
-    gy, act = p.meta["grad_y"], p.meta["act"]
-    qa, sa = synth.quant_rows_1x128(gy.t().contiguous(), "ue8m0")  # [M, T] rows = channels
-    qb, sb = synth.quant_rows_1x128(act.t().contiguous(), "ue8m0")
-    A = torch.cat([qa[:, 0:128].reshape(-1), qa[:, 128:512].reshape(-1)])
-    B = torch.cat([qb[:, 0:128].reshape(-1), qb[:, 128:512].reshape(-1)])
-    pu = synth.Problem("kgrouped", "fp8", 2, 128, 512, A, B, sa, sb, "ue8m0", "channel",
-                       M=128, K_total=512, ks=p.ks, meta={"ks": np.array(ks)})
-    D = run_kgrouped(pu, None, accumulate=False)
+@pytest.mark.parametrize("sf_val", [1.0, 1e-30])
+def test_kgrouped_ue8m0_scales(sf_val):
+    """Power-of-two per-channel scales on both operands (the repro's zeroed channel
+    included, so all-zero groups take the UE8M0 code of sf_val), with and without
+    accumulation onto a random C: element-wise bound, calc_diff and exact zeros."""
+    ks = [128, 384, 0, 256]
+    say("kgrouped ue8m0", ks, sf_val)
+    p = synth.make_kgrouped("fp8", ks, 192, 136, seed=9, std_a=1.0, std_b=1.0, device=DEV,
+                            sf_val=sf_val, sf_fmt="ue8m0")
+    assert p.SFA.dtype == torch.uint8
+    D = run_kgrouped(p, None, accumulate=False)
     torch.cuda.synchronize()
-    Dh = D.cpu().numpy()
-    ref, _ = oracle.grouped_gemm_kgrouped("fp8", A.cpu().numpy(), B.cpu().numpy(), ks, 128, 128,
-                                          512, sa.cpu().numpy(), sb.cpu().numpy(), "ue8m0")
-    assert oracle.calc_diff(Dh, ref) < 1e-3
-    assert np.allclose(Dh, ref, rtol=1e-3, atol=1e-4 * np.abs(ref).max())
+    assert (D[0, 0] == 0).all(), "the zeroed channel gives exact zeros"
+    assert_report(check_kgrouped(p, D), "fp8")
+    C = torch.randn((p.G, p.M, p.N), device=DEV)
+    D2 = C.clone()
+    run_kgrouped(p, D2, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(D2[2], C[2]), "k_e = 0 with accumulation leaves D_e unchanged"
+    assert_report(check_kgrouped(p, D2, C=C), "fp8")
 
 
 # ----------------------------------------------------------------------------- prefix sums

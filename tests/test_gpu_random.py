@@ -81,17 +81,18 @@ def k_cases(n=16, seed=77):
         ks = [gran * int(rng.integers(0, 5 if dt == "fp8" else 60)) for _ in range(G)]
         out.append(dict(case=c, dt=dt, ks=ks, M=8 * int(rng.integers(1, 41)),
                         N=8 * int(rng.integers(1, 41)), acc=int(rng.integers(0, 2)),
-                        seed=int(rng.integers(1 << 30))))
+                        seed=int(rng.integers(1 << 30)),
+                        sf="ue8m0" if dt == "fp8" and (c // 2) % 2 else "f32"))
     return out
 
 
-@pytest.mark.parametrize("cfg", k_cases(), ids=lambda c: f"k{c['case']}-{c['dt']}")
+@pytest.mark.parametrize("cfg", k_cases(), ids=lambda c: f"k{c['case']}-{c['dt']}-{c['sf']}")
 def test_random_k_grouped(cfg):
     say("random", cfg)
     if sum(cfg["ks"]) == 0:
         cfg = dict(cfg, ks=[128 if cfg["dt"] == "fp8" else 8] + cfg["ks"][1:])
     p = synth.make_kgrouped(cfg["dt"], cfg["ks"], cfg["M"], cfg["N"], cfg["seed"], DEV,
-                            std_a=1.0, std_b=1.0)
+                            std_a=1.0, std_b=1.0, sf_fmt=cfg["sf"])
     g = torch.Generator(device=DEV).manual_seed(cfg["seed"])
     C = torch.randn((p.G, p.M, p.N), device=DEV, generator=g)
     D = C.clone()
