@@ -24,6 +24,10 @@
  *
  * Common rules for every entry point:
  *  - Every pointer is caller-owned device memory; the caller allocates every output.
+ *  - Sizes: operands and outputs may exceed 2 GiB. What must stay below 2 GiB is 128 rows of
+ *    an activation, output or K-grouped operand, 256 weight rows (the fused SwiGLU call:
+ *    one expert's 2I weight rows), and each scale and routing tensor; otherwise
+ *    MGG_EUNSUPPORTED.
  *  - The call validates its host arguments first. On any violation it returns an error
  *    code and enqueues nothing.
  *  - Otherwise it enqueues kernels on `stream` and returns without synchronizing. It

@@ -42,8 +42,10 @@ using TileL = Tile<128, 256, 2, 2, 3>;   // larger experts, BF16
 // MFMA-bound 6 x 4096 x 4096 shape; BF16 is better served by four)
 using TileL8 = Tile<128, 256, 2, 4, 3>;
 // the fused SwiGLU tile: 128 output columns (their gate and up weight rows), eight waves
-// of 16 rows x all 256 weight rows
+// of 16 rows x all 256 weight rows; the two-stage form takes over when the row-block table
+// of a long contiguous layout (beyond ~2900 blocks) no longer fits next to three stages
 using TileSwi = Tile<128, 256, 8, 1, 3, true>;
+using TileSwi2 = Tile<128, 256, 8, 1, 2, true>;
 using TileK = Tile<64, 128, 2, 2, 3>;    // K-grouped output tiles
 
 enum TileId { kTileS = 0, kTileM = 1, kTileL = 2 };
@@ -181,6 +183,15 @@ mgg_status dispatch_m(mgg_dtype dt, mgg_sf_fmt sf, mgg_sfb_gran gran, TileId til
   return launch_tile<VAR, kFP8, kSfUE8M0, kSfbChannel>(tile, p, s);
 }
 
+// The fused SwiGLU tile with three stages, or with two when the contiguous layout's
+// row-block table does not fit next to three (the bits are the same either way).
+template <int DT, int SF, int GRAN>
+mgg_status launch_swi(const Params& p, hipStream_t s) {
+  if (lds_bytes<TileSwi, kContig, DT, SF, GRAN, false>(p) <= kLdsBytes)
+    return launch<TileSwi, kContig, DT, SF, GRAN, false>(p, m_tiles<TileSwi, kContig>(p), s);
+  return launch<TileSwi2, kContig, DT, SF, GRAN, false>(p, m_tiles<TileSwi2, kContig>(p), s);
+}
+
 TileId pick_tile(int expected_m, int fallback) {
   const int em = expected_m > 0 ? expected_m : fallback;
   if (em <= 32) return kTileS;
@@ -190,9 +201,14 @@ TileId pick_tile(int expected_m, int fallback) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Every buffer the kernels address must be below 2 GiB so that a 32-bit out-of-range
-// offset can mask a lane.
+// Every buffer resource the kernels address must be below 2 GiB so that a 32-bit
+// out-of-range offset can mask a lane. Operand and output resources start at a tile's
+// first row, so the limit applies to one tile's rows (at most kTileRowsA activation or
+// output rows, kTileRowsB weight rows; the fused SwiGLU tile gathers its weight rows from
+// the whole expert), while scale and routing tensors are addressed whole.
 constexpr long kMaxBuffer = (1L << 31) - 1;
+constexpr long kTileRowsA = 128;
+constexpr long kTileRowsB = 256;
 
 uint32_t scale_bytes(long count, mgg_sf_fmt sf) {
   // UE8M0 buffers are read in whole dwords: the caller's allocation must be readable up
@@ -311,7 +327,7 @@ mgg_status grouped_gemm_masked(mgg_dtype dt, int G, int cap, int N, int K, const
   if (st != MGG_OK) return st;
   const long esz = dt == MGG_BF16 ? 2 : 1, KB = K / 128;
   const long sfa_n = (long)G * KB * cap;
-  st = check_sizes({(long)cap * K * esz, (long)N * b_row, (long)cap * N * 2, sfa_n * 4,
+  st = check_sizes({kTileRowsA * K * esz, kTileRowsB * b_row, kTileRowsA * N * 2, sfa_n * 4,
                     sfb_n * 4, (long)G * cdiv(cap, 32) * cdiv(N, 64)});
   if (st != MGG_OK) return st;
   Params p{};
@@ -347,7 +363,8 @@ mgg_status grouped_gemm_contiguous(mgg_dtype dt, int G, int M, int N, int K, con
   if (st != MGG_OK) return st;
   const long esz = dt == MGG_BF16 ? 2 : 1, KB = K / 128;
   const long sfa_n = KB * M;
-  st = check_sizes({(long)M * K * esz, (long)N * b_row, (long)M * N * 2, sfa_n * 4, sfb_n * 4});
+  st = check_sizes({kTileRowsA * K * esz, kTileRowsB * b_row, kTileRowsA * N * 2, sfa_n * 4,
+                    sfb_n * 4});
   if (st != MGG_OK) return st;
   Params p{};
   p.A = (const uint8_t*)A;
@@ -381,8 +398,8 @@ mgg_status grouped_gemm_contiguous_psum(mgg_dtype dt, int G, int M, int N, int K
   if (st != MGG_OK) return st;
   const long esz = dt == MGG_BF16 ? 2 : 1, KB = K / 128;
   const long sfa_n = KB * M;
-  st = check_sizes({(long)M * K * esz, (long)N * b_row, (long)M * N * 2, sfa_n * 4, sfb_n * 4,
-                    (cdiv(M, 32) + G) * cdiv(N, 64)});
+  st = check_sizes({kTileRowsA * K * esz, kTileRowsB * b_row, kTileRowsA * N * 2, sfa_n * 4,
+                    sfb_n * 4, (cdiv(M, 32) + G) * cdiv(N, 64)});
   if (st != MGG_OK) return st;
   Params p{};
   p.A = (const uint8_t*)A;
@@ -430,7 +447,8 @@ mgg_status grouped_gemm_contiguous_swiglu_quant(mgg_dtype dt, int G, int M, int 
   if (st != MGG_OK) return st;
   const long KB = K / 128;
   const long sfa_n = KB * M, sfq_n = (long)(I / 128) * M;
-  st = check_sizes({(long)M * K, 2L * I * b_row, (long)M * I, sfa_n * 4, sfb_n * 4, sfq_n * 4});
+  st = check_sizes({kTileRowsA * K, 2L * I * b_row, kTileRowsA * I, sfa_n * 4, sfb_n * 4,
+                    sfq_n * 4});
   if (st != MGG_OK) return st;
   Params p{};
   p.A = (const uint8_t*)A;
@@ -450,14 +468,11 @@ mgg_status grouped_gemm_contiguous_swiglu_quant(mgg_dtype dt, int G, int M, int 
   p.sfq_ue8m0 = sfq == MGG_SF_UE8M0;
   p.sf_zero = sf_zero;
   p.sfq_bytes = scale_bytes(sfq_n, sfq);
-  const long tiles = m_tiles<TileSwi, kContig>(p);
   if (dt == MGG_FP8_FP4)
-    return launch<TileSwi, kContig, kFP4W, kSfUE8M0, kSfbBlock32, false>(p, tiles, stream);
-  if (sf == MGG_SF_UE8M0)
-    return launch<TileSwi, kContig, kFP8, kSfUE8M0, kSfbBlock, false>(p, tiles, stream);
-  if (gran == MGG_SFB_BLOCK128)
-    return launch<TileSwi, kContig, kFP8, kSfF32, kSfbBlock, false>(p, tiles, stream);
-  return launch<TileSwi, kContig, kFP8, kSfF32, kSfbChannel, false>(p, tiles, stream);
+    return launch_swi<kFP4W, kSfUE8M0, kSfbBlock32>(p, stream);
+  if (sf == MGG_SF_UE8M0) return launch_swi<kFP8, kSfUE8M0, kSfbBlock>(p, stream);
+  if (gran == MGG_SFB_BLOCK128) return launch_swi<kFP8, kSfF32, kSfbBlock>(p, stream);
+  return launch_swi<kFP8, kSfF32, kSfbChannel>(p, stream);
 }
 
 mgg_status grouped_gemm_kgrouped(mgg_dtype dt, int G, int M, int N, int K_total, const void* A,
@@ -495,7 +510,7 @@ mgg_status kgrouped_impl(mgg_dtype dt, int G, int M, int N, int K_total, const v
   if (accumulate != 0 && accumulate != 1) return fail(MGG_EINVAL, "accumulate must be 0 or 1");
   const long esz = dt == MGG_FP8_E4M3 ? 1 : 2, KB = K_total / 128;
   const long tiles = (long)G * cdiv(M, TileK::BM) * cdiv(N, TileK::BN);
-  st = check_sizes({(long)M * K_total * esz, (long)N * K_total * esz, (long)M * N * 4,
+  st = check_sizes({kTileRowsA * K_total * esz, kTileRowsB * K_total * esz, kTileRowsA * N * 4,
                     KB * M * 4, KB * N * 4, tiles});
   if (st != MGG_OK) return st;
   Params p{};

@@ -39,17 +39,18 @@ struct TileCtx {
   int k_bytes;   // bytes of K in an activation row (0: nothing to load; FP4 weights: half)
   int a_lim;     // activation rows < a_lim are loaded (others read as zero)
   int row_end;   // masked: valid rows end; contiguous/K-grouped: M
-  const uint8_t* a_base;  // expert's activation block
-  uint32_t a_bytes;
-  const uint8_t* b_base;  // expert's weight block
+  const uint8_t* a_base;  // the tile's first activation row (row m0)
+  uint32_t a_bytes;       // bytes of the tile's rows that exist in the operand
+  const uint8_t* b_base;  // weight rows from b_row0 on (this n-tile's, or the expert's)
   uint32_t b_bytes;
+  int b_row0;             // weight row at b_base
   int lda, ldb;  // row strides in bytes
   long sfa_off;  // element offset of scale group 0, row 0
   int sfa_ld;    // elements between consecutive scale groups
   long sfb_off;
   int sfb_ld;
-  uint8_t* d_base;  // expert's output block
-  uint32_t d_bytes;
+  uint8_t* d_base;  // the tile's first output row (row m0)
+  uint32_t d_bytes; // bytes of the tile's output rows that exist
 };
 
 template <class T, int VAR>
@@ -275,14 +276,18 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       t.nk = (Kb + kSliceBytes - 1) / kSliceBytes;
       t.a_lim = c;
       t.row_end = c;
-      // masked: expert g's block of cap rows; psum: its segment of the [M] rows
+      // masked: expert g's block of cap rows; psum: its segment of the [M] rows. Buffer
+      // resources start at the tile's first row (and first weight row), so 32-bit offsets
+      // never span more than one tile whatever the operand sizes.
       const long r0 = VAR == kPsum ? (long)S.s_c[g] : (long)g * p.rows;
       const long rn = VAR == kPsum ? (long)c : (long)p.rows;
+      const long rt = min((long)T::BM, rn - t.m0);  // rows of the block from m0 on
       const int Kbw = DT == kFP4W ? Kb / 2 : Kb;  // weight bytes per row
-      t.a_base = p.A + r0 * Kb;
-      t.a_bytes = (uint32_t)(rn * Kb);
-      t.b_base = p.B + (long)g * p.N * Kbw;
-      t.b_bytes = (uint32_t)((long)p.N * Kbw);
+      t.a_base = p.A + (r0 + t.m0) * Kb;
+      t.a_bytes = (uint32_t)(rt * Kb);
+      t.b_row0 = T::SWI ? 0 : t.n0;
+      t.b_base = p.B + ((long)g * p.N + t.b_row0) * Kbw;
+      t.b_bytes = (uint32_t)((T::SWI ? (long)p.N : min((long)T::BN, (long)(p.N - t.n0))) * Kbw);
       t.lda = Kb;
       t.ldb = Kbw;
       t.sfa_off = VAR == kPsum ? r0 : (long)g * KB * p.rows;
@@ -294,8 +299,8 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
         t.sfb_off = (long)g * KB * p.N;
         t.sfb_ld = p.N;
       }
-      t.d_base = reinterpret_cast<uint8_t*>(p.D) + r0 * p.N * 2;
-      t.d_bytes = (uint32_t)(rn * p.N * 2);
+      t.d_base = reinterpret_cast<uint8_t*>(p.D) + (r0 + t.m0) * p.N * 2;
+      t.d_bytes = (uint32_t)(rt * p.N * 2);
     }
   } else if constexpr (VAR == kContig) {
     constexpr int SUB = kContigBlock / T::BM;
@@ -319,11 +324,13 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       t.nk = (Kb + kSliceBytes - 1) / kSliceBytes;
       t.a_lim = p.rows;
       t.row_end = p.rows;
+      const long rt = min((long)T::BM, (long)(p.rows - m0));  // rows of the tile that exist
       const int Kbw = DT == kFP4W ? Kb / 2 : Kb;  // weight bytes per row
-      t.a_base = p.A;
-      t.a_bytes = (uint32_t)((long)p.rows * Kb);
-      t.b_base = p.B + (long)e * p.N * Kbw;
-      t.b_bytes = (uint32_t)((long)p.N * Kbw);
+      t.a_base = p.A + (long)m0 * Kb;
+      t.a_bytes = (uint32_t)(rt * Kb);
+      t.b_row0 = T::SWI ? 0 : t.n0;
+      t.b_base = p.B + ((long)e * p.N + t.b_row0) * Kbw;
+      t.b_bytes = (uint32_t)((T::SWI ? (long)p.N : min((long)T::BN, (long)(p.N - t.n0))) * Kbw);
       t.lda = Kb;
       t.ldb = Kbw;
       t.sfa_off = 0;
@@ -335,9 +342,10 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
         t.sfb_off = (long)e * KB * p.N;
         t.sfb_ld = p.N;
       }
-      t.d_base = reinterpret_cast<uint8_t*>(p.D);
       // bf16 [rows][N]; the fused SwiGLU tile writes E4M3 codes [rows][N/2]
-      t.d_bytes = (uint32_t)((long)p.rows * (T::SWI ? p.N / 2 : p.N * 2));
+      const long ldd = T::SWI ? p.N / 2 : (long)p.N * 2;
+      t.d_base = reinterpret_cast<uint8_t*>(p.D) + (long)m0 * ldd;
+      t.d_bytes = (uint32_t)(rt * ldd);
       break;
     }
   } else {
@@ -362,17 +370,21 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       t.nk = t.k_bytes > 0 ? (t.k_bytes + kSliceBytes - 1) / kSliceBytes : 1;
       t.a_lim = p.rows;
       t.row_end = p.rows;
-      t.a_base = p.A + (long)p.rows * pe * esz;
-      t.a_bytes = (uint32_t)((long)p.rows * k * esz);
-      t.b_base = p.B + (long)p.N * pe * esz;
-      t.b_bytes = (uint32_t)((long)p.N * k * esz);
+      const long rt = min((long)T::BM, (long)(p.rows - t.m0));
+      const long ct = min((long)T::BN, (long)(p.N - t.n0));
+      // expert e's blocks [M][k_e] and [N][k_e], entered at the tile's first row
+      t.a_base = p.A + ((long)p.rows * pe + (long)t.m0 * k) * esz;
+      t.a_bytes = (uint32_t)(rt * k * esz);
+      t.b_row0 = t.n0;
+      t.b_base = p.B + ((long)p.N * pe + (long)t.n0 * k) * esz;
+      t.b_bytes = (uint32_t)(ct * k * esz);
       t.lda = t.ldb = k * esz;
       t.sfa_off = (pe / 128) * p.rows;
       t.sfa_ld = p.rows;
       t.sfb_off = (pe / 128) * p.N;
       t.sfb_ld = p.N;
-      t.d_base = reinterpret_cast<uint8_t*>(p.D) + (long)e * p.rows * p.N * 4;
-      t.d_bytes = (uint32_t)((long)p.rows * p.N * 4);
+      t.d_base = reinterpret_cast<uint8_t*>(p.D) + ((long)e * p.rows + t.m0) * p.N * 4;
+      t.d_bytes = (uint32_t)(rt * p.N * 4);
       break;
     }
   }
@@ -406,7 +418,7 @@ __device__ __forceinline__ void accumulate_waves(const Sched<T, VAR>& Sd, const 
   }
   auto offset = [&](const TileCtx& t, int u) -> uint32_t {
     const int m = t.m0 + rr[u], n = t.n0 + 4 * cc[u];
-    return (t.valid && m < p.rows && n < p.N) ? (uint32_t)(((long)m * p.N + n) * 4) : kOOB;
+    return (t.valid && m < p.rows && n < p.N) ? (uint32_t)(((long)rr[u] * p.N + n) * 4) : kOOB;
   };
   v4i ring[P][PER];
   TileCtx tp = t0;  // prefetch cursor, P tiles ahead of te
@@ -540,7 +552,7 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
       const int R = 8 * (4 * u + cwave) + (lane >> 3);
       if (u < Lay::U_A) {
         const int m = t.m0 + R;
-        I.vab[u] = (t.valid && m < t.a_lim) ? (uint32_t)(m * t.lda + c16) : kOOB;
+        I.vab[u] = (t.valid && m < t.a_lim) ? (uint32_t)(R * t.lda + c16) : kOOB;
       } else if constexpr (Lay::FP4W) {
         // 16 weight rows of 64 bytes per copy; chunk c of LDS row Rb sits at position
         // c ^ ((Rb / 2) % 4), so 8 consecutive rows read at one logical chunk hit 8
@@ -549,11 +561,11 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
         const int lc = (lane & 3) ^ ((Rb >> 1) & 3);
         int n;
         const bool ok = weight_row(t, weight_row_of_lds<T, false>(Rb), n);
-        I.vab[u] = (t.valid && ok) ? (uint32_t)(n * t.ldb + 16 * lc) : kOOB;
+        I.vab[u] = (t.valid && ok) ? (uint32_t)((n - t.b_row0) * t.ldb + 16 * lc) : kOOB;
       } else {
         int n;
         const bool ok = weight_row(t, weight_row_of_lds<T, !FP8>(R - T::BM), n);
-        I.vab[u] = (t.valid && ok) ? (uint32_t)(n * t.ldb + c16) : kOOB;
+        I.vab[u] = (t.valid && ok) ? (uint32_t)((n - t.b_row0) * t.ldb + c16) : kOOB;
       }
     }
   };
@@ -911,7 +923,7 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
           const float* v = x[4 * q + e];
           w[e] = (int)to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
         }
-        const uint32_t voff = row_ok ? (uint32_t)((long)m * I + col + 16 * q) : kOOB;
+        const uint32_t voff = row_ok ? (uint32_t)((long)rl * I + col + 16 * q) : kOOB;
         store_b128(rs_d, voff, w);
       }
       const v4i rs_q = make_rsrc(p.SFQ, p.sfq_bytes);
@@ -943,7 +955,7 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
               continue;
             }
             const bool ok = row_ok && n_start + 4 * i + 4 <= p.N;
-            const uint32_t voff = ok ? (uint32_t)(((long)m * p.N + n_start + 4 * i) * 4) : kOOB;
+            const uint32_t voff = ok ? (uint32_t)(((long)rl * p.N + n_start + 4 * i) * 4) : kOOB;
             store_b128(rs_d, voff, (v4i){__float_as_int(v[0]), __float_as_int(v[1]),
                                          __float_as_int(v[2]), __float_as_int(v[3])});
           }
@@ -954,7 +966,7 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
             const v4i w = {(int)pack_bf16x2(x[0], x[1]), (int)pack_bf16x2(x[2], x[3]),
                            (int)pack_bf16x2(y[0], y[1]), (int)pack_bf16x2(y[2], y[3])};
             const bool ok = row_ok && n_start + 8 * h + 8 <= p.N;
-            const uint32_t voff = ok ? (uint32_t)(((long)m * p.N + n_start + 8 * h) * 2) : kOOB;
+            const uint32_t voff = ok ? (uint32_t)(((long)rl * p.N + n_start + 8 * h) * 2) : kOOB;
             store_b128(rs_d, voff, w);
           }
         }
@@ -985,7 +997,7 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
                 continue;
               }
               const bool ok = row_ok && n_start + 4 * q + 4 <= p.N;
-              const uint32_t voff = ok ? (uint32_t)(((long)m * p.N + n_start + 4 * q) * 4) : kOOB;
+              const uint32_t voff = ok ? (uint32_t)(((long)rl * p.N + n_start + 4 * q) * 4) : kOOB;
               store_b128(rs_d, voff, (v4i){__float_as_int(x[0]), __float_as_int(x[1]),
                                            __float_as_int(x[2]), __float_as_int(x[3])});
             }
@@ -997,7 +1009,7 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
                              (int)pack_bf16x2(v[8 * h + 4], v[8 * h + 5]),
                              (int)pack_bf16x2(v[8 * h + 6], v[8 * h + 7])};
               const bool ok = row_ok && n_start + 8 * h + 8 <= p.N;
-              const uint32_t voff = ok ? (uint32_t)(((long)m * p.N + n_start + 8 * h) * 2) : kOOB;
+              const uint32_t voff = ok ? (uint32_t)(((long)rl * p.N + n_start + 8 * h) * 2) : kOOB;
               store_b128(rs_d, voff, w);
             }
           }

@@ -1,7 +1,7 @@
 """GPU parity at the library's documented maximum sizes: 4096 experts (every M-grouped
 layout and the K-grouped one), the contiguous layout's 4096 row blocks (524288 rows, one
-expert per block), an activation operand one row block short of 2 GiB (the largest byte
-offsets a 32-bit buffer offset addresses), and expert counts whose scheduler tables push
+expert per block), activation operands and outputs beyond 2 GiB in every layout (buffer
+resources start at each tile's first row), and expert counts whose scheduler tables push
 the largest tiles out of LDS (the host then falls back to a smaller tile, which must give
 the same bits). Oracle checks use sampled rows where the full output is large; every
 padding row is checked to keep its sentinel."""
@@ -124,3 +124,101 @@ def test_kgrouped_max_experts(dt):
     run_kgrouped(p, D, accumulate=True)
     torch.cuda.synchronize()
     assert_report(check_kgrouped(p, D, C=C), dt)
+
+
+# ----------------------------------------------------------------------------- beyond 2 GiB
+# Operand and output buffer resources start at each tile's first row, so tensors larger
+# than 2 GiB are addressed with 32-bit offsets that never span more than one tile.
+
+
+def test_contiguous_activations_beyond_2gib():
+    """A = 524288 x 7168 FP8 bytes (3.76 GB, M K > 2^31), 8 experts with long segments, the
+    last ending on the last row; sampled rows (every segment's first and last included)
+    against the oracle and the sentinel on every padding row."""
+    M, K, N, G = MAX_CONTIG_ROWS, 7168, 64, 8
+    rng = np.random.default_rng(16)
+    head = rng.integers(30000, 70000, size=G - 1)
+    padded = int(sum((s + 127) // 128 * 128 for s in head))
+    segs = np.concatenate([head, [M - padded]])
+    say("contiguous A beyond 2 GiB", segs.tolist())
+    p = synth.make_contiguous("fp8", G, N, K, segs, seed=16, device=DEV, M_max=M)
+    assert p.A.numel() == M * K and p.A.numel() > 2 ** 31
+    D = sentinel_like((M, N), DEV)
+    run_contiguous(p, 113, D)
+    torch.cuda.synchronize()
+    idx = p.meta["m_indices"]
+    valid = np.nonzero(idx >= 0)[0]
+    starts = np.nonzero(np.diff(np.concatenate([[-2], idx])) != 0)[0]
+    ends = np.nonzero(np.diff(np.concatenate([idx, [-2]])) != 0)[0]
+    edges = [r for r in np.concatenate([starts, ends]) if idx[r] >= 0]
+    rows = sample_rows(valid, 192, 3, must=edges + [M - 1])
+    assert_report(check_contiguous(p, D, rows=rows), "fp8")
+
+
+def test_contiguous_output_beyond_2gib():
+    """D = 524288 x 2304 bf16 (2.4 GB, M N 2 > 2^31), BF16 operands with K = 64."""
+    M, K, N, G = MAX_CONTIG_ROWS, 64, 2304, 4
+    segs = np.array([150000, 1, 200000, M - 350208])
+    say("contiguous D beyond 2 GiB", segs.tolist())
+    p = synth.make_contiguous("bf16", G, N, K, segs, seed=17, device=DEV, M_max=M)
+    D = sentinel_like((M, N), DEV)
+    assert D.numel() * 2 > 2 ** 31
+    run_contiguous(p, 128, D)
+    torch.cuda.synchronize()
+    valid = np.nonzero(p.meta["m_indices"] >= 0)[0]
+    rows = sample_rows(valid, 128, 4, must=(0, 149999, 150016, 150144, valid[-1], M - 1))
+    assert_report(check_contiguous(p, D, rows=rows), "bf16")
+
+
+def test_psum_segment_beyond_2gib():
+    """One prefix-sum segment of 300000 rows x K = 7168 (2.15 GB of activations), five
+    unrouted tail rows; sampled rows against the oracle (through the per-row expert view of
+    the same segments) and the sentinel on the tail."""
+    G, K, N = 3, 7168, 64
+    segs = [1000, 300000, 77]
+    say("psum segment beyond 2 GiB", segs)
+    p = synth.make_contiguous_psum("fp8", G, N, K, segs, seed=18, device=DEV, sf_fmt="ue8m0",
+                                   tail=5)
+    assert segs[1] * K > 2 ** 31
+    D = sentinel_like((p.M, N), DEV)
+    run_psum(p, 200, D)
+    torch.cuda.synchronize()
+    ends = np.cumsum(segs)
+    idx = np.full(p.M, -1, np.int32)
+    for e, (r0, r1) in enumerate(zip(np.concatenate([[0], ends[:-1]]), ends)):
+        idx[r0:r1] = e
+    rows = sample_rows(np.arange(ends[-1]), 160, 5,
+                       must=(0, 999, 1000, 1001, 300999, 301000, ends[-1] - 1))
+    view = synth.Problem("contiguous", "fp8", G, N, K, p.A, p.B, p.SFA, p.SFB, p.sf_fmt,
+                         p.sfb_gran, M=p.M, meta={"m_indices": idx})
+    assert_report(check_contiguous(view, D, rows=rows), "fp8")
+
+
+def test_masked_expert_block_beyond_2gib():
+    """One expert of capacity 131200 x K = 16384 FP8 (2.15 GB), all rows valid but the last."""
+    G, cap, N, K = 1, 131200, 64, 16384
+    counts = [cap - 1]
+    say("masked expert block beyond 2 GiB")
+    p = synth.make_masked("fp8", G, cap, N, K, counts, seed=19, device=DEV)
+    assert cap * K > 2 ** 31
+    D = run_masked(p, 4096)
+    torch.cuda.synchronize()
+    rows = {0: list(sample_rows(np.arange(cap - 1), 128, 6, must=(0, 1, cap - 3, cap - 2)))}
+    assert_report(check_masked(p, D, experts=[0], rows=rows), "fp8")
+
+
+def test_kgrouped_output_beyond_2gib():
+    """K-grouped with M = N = 24576: the expert's fp32 output is 2.4 GB; sampled rows and
+    columns (the first and last of each included) against the oracle."""
+    M = N = 24576
+    ks = [256]
+    say("kgrouped D beyond 2 GiB")
+    p = synth.make_kgrouped("fp8", ks, M, N, seed=20, device=DEV, std_a=1.0, std_b=1.0)
+    D = torch.zeros((1, M, N), device=DEV)
+    assert D.numel() * 4 > 2 ** 31
+    run_kgrouped(p, D, accumulate=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([rng.choice(M, 48, replace=False), [0, 1, M - 2, M - 1]]))
+    cols = np.unique(np.concatenate([rng.choice(N, 48, replace=False), [0, 1, N - 2, N - 1]]))
+    assert_report(check_kgrouped(p, D, rows=rows, cols=cols), "fp8")

@@ -304,6 +304,29 @@ def test_fused_swiglu_full_w13_shape():
     assert_fused_plain(H, Qf, SFf, valid, "ue8m0")
 
 
+# Row blocks at which the three-stage fused tile's scheduler table (4 bytes per 128-row
+# block, after three 50 176 .. 51 200-byte pipeline stages) still fits in 160 KB of LDS:
+# float32 scales with 128 x 128 weight blocks 2944, with per-channel weight scales 2560.
+# One block more and the host falls back to the two-stage tile; 4096 blocks (524288 rows)
+# is the contiguous layout's maximum.
+@pytest.mark.parametrize("gran,blocks", [("block128", 2944), ("block128", 2945),
+                                         ("channel", 2560), ("channel", 2561),
+                                         ("block128", 4096)])
+def test_fused_swiglu_row_block_limits(gran, blocks):
+    """Either side of the fused tile's LDS limit and at the layout's maximum rows: every
+    routed row bit-identical to the separate steps, untouched rows keep their fill."""
+    M = blocks * 128
+    rng = np.random.default_rng(blocks)
+    segs = rng.integers(0, 129, size=blocks - 1)
+    segs[-1] = 128
+    say("fused row blocks", gran, blocks)
+    p = synth.make_contiguous("fp8", int(segs.size), 256, 256, segs, seed=52, device=DEV,
+                              sf_fmt="f32", sfb_gran=gran, M_max=M, std_b=0.05)
+    assert p.M == M
+    Qf, SFf, Qs, SFs, valid, H = fused_vs_separate(p, "f32")
+    assert_fused_equal(Qf, SFf, Qs, SFs, valid)
+
+
 def test_fused_chain_graph_replay_changing_routing():
     """Fused w13 + w2 captured in one graph and replayed with new routing values: every
     replay equals the eager chain and the separate steps, and the oracle chain within the
