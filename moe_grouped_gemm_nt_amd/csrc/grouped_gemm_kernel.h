@@ -35,6 +35,7 @@ struct TileCtx {
   int valid;     // 0 once the workgroup has no more tiles
   int g;         // expert
   int m0, n0;    // first activation row / weight row of the tile
+  int n_end;     // end of the tile's weight rows (output columns): min(N, n0 + BN)
   int nk;        // 128-byte K slices to run (at least 1)
   int k_bytes;   // bytes of K in an activation row (0: nothing to load; FP4 weights: half)
   int a_lim;     // activation rows < a_lim are loaded (others read as zero)
@@ -272,22 +273,23 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       t.g = g;
       t.m0 = mt * T::BM;
       t.n0 = nt * T::BN;
+      t.n_end = T::SWI ? p.N : min(p.N, t.n0 + T::BN);
       t.k_bytes = Kb;
       t.nk = (Kb + kSliceBytes - 1) / kSliceBytes;
       t.a_lim = c;
       t.row_end = c;
       // masked: expert g's block of cap rows; psum: its segment of the [M] rows. Buffer
       // resources start at the tile's first row (and first weight row), so 32-bit offsets
-      // never span more than one tile whatever the operand sizes.
+      // never span more than one tile whatever the operand sizes, and end at its last
+      // valid row: the padding rows of a masked block read as zeros without being fetched.
       const long r0 = VAR == kPsum ? (long)S.s_c[g] : (long)g * p.rows;
-      const long rn = VAR == kPsum ? (long)c : (long)p.rows;
-      const long rt = min((long)T::BM, rn - t.m0);  // rows of the block from m0 on
+      const long rt = min((long)T::BM, (long)c - t.m0);  // valid rows of the tile
       const int Kbw = DT == kFP4W ? Kb / 2 : Kb;  // weight bytes per row
       t.a_base = p.A + (r0 + t.m0) * Kb;
       t.a_bytes = (uint32_t)(rt * Kb);
       t.b_row0 = T::SWI ? 0 : t.n0;
       t.b_base = p.B + ((long)g * p.N + t.b_row0) * Kbw;
-      t.b_bytes = (uint32_t)((T::SWI ? (long)p.N : min((long)T::BN, (long)(p.N - t.n0))) * Kbw);
+      t.b_bytes = (uint32_t)((T::SWI ? (long)p.N : (long)(t.n_end - t.n0)) * Kbw);
       t.lda = Kb;
       t.ldb = Kbw;
       t.sfa_off = VAR == kPsum ? r0 : (long)g * KB * p.rows;
@@ -320,6 +322,7 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       t.g = e;
       t.m0 = m0;
       t.n0 = nt * T::BN;
+      t.n_end = T::SWI ? p.N : min(p.N, t.n0 + T::BN);
       t.k_bytes = Kb;
       t.nk = (Kb + kSliceBytes - 1) / kSliceBytes;
       t.a_lim = p.rows;
@@ -366,6 +369,7 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       t.g = e;
       t.m0 = mt * T::BM;
       t.n0 = nt * T::BN;
+      t.n_end = min(p.N, t.n0 + T::BN);
       t.k_bytes = k * esz;
       t.nk = t.k_bytes > 0 ? (t.k_bytes + kSliceBytes - 1) / kSliceBytes : 1;
       t.a_lim = p.rows;
@@ -653,18 +657,11 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
       // accumulates into the tile accumulator, so no promotion instructions are needed:
       // the weight scale goes with the first operand (weight rows), the activation
       // scale with the second (activation rows).
-      v8i bfr[MJ];
+      // Scale bytes first (see the float32-scale path below for the order of the rest).
       int sab[MJ];
       const long oa = t.sfa_off + (long)s * t.sfa_ld + t.m0;
 #pragma unroll
-      for (int j = 0; j < MJ; ++j) {
-        const int row = wm0 + 16 * j + lr;
-        const uint8_t* rp = st + Lay::A_OFF + row * kSliceBytes;
-        const v4i lo = *reinterpret_cast<const v4i*>(rp + x_lo);
-        const v4i hi = *reinterpret_cast<const v4i*>(rp + x_hi);
-        bfr[j] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        sab[j] = st[Lay::SA_OFF + (int)(oa & 3) + row];
-      }
+      for (int j = 0; j < MJ; ++j) sab[j] = st[Lay::SA_OFF + (int)(oa & 3) + wm0 + 16 * j + lr];
       int sbw = 0, sbw2 = 0;  // block scale of the wave's rows (fused tile: gate, up)
       if constexpr (GRAN == kSfbBlock) {
         if constexpr (T::SWI) {
@@ -678,6 +675,13 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
           sbw = st[Lay::SB_OFF + 4 * lb + (int)(ob & 3)];
         }
       }
+      // Activation fragment j: 16 rows x 128 K of the wave's rows.
+      auto load_a = [&](int j, v8i& b) {
+        const uint8_t* rp = st + Lay::A_OFF + (wm0 + 16 * j + lr) * kSliceBytes;
+        const v4i lo = *reinterpret_cast<const v4i*>(rp + x_lo);
+        const v4i hi = *reinterpret_cast<const v4i*>(rp + x_hi);
+        b = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      };
       // Weight fragment i and the scale of the weight row this lane supplies.
       auto load_w = [&](int i, v8i& afr, int& sb) {
         const int R = wn0 + 16 * i + lr;
@@ -701,45 +705,50 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
           }
         }
       };
+      v8i bfr[MJ];
       v8i wf[3];
       int sw[3];
+      auto mfma = [&](int i, int j) {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            wf[i % 3], bfr[j], acc[i][j], kFmtW, 0, 0, sw[i % 3], 0, sab[j]);
+      };
+      constexpr int NA = MJ > 2 ? MJ - 2 : 0;  // activation reads behind the first group
+      constexpr int NW = NI - 1 < 2 ? NI - 1 : 2;  // weight reads behind it
+      auto later_read = [&](int q) {
+        if (q < NA) load_a(q + 2, bfr[q + 2]);
+        else if (q - NA < NW) load_w(q - NA + 1, wf[q - NA + 1], sw[q - NA + 1]);
+      };
       load_w(0, wf[0], sw[0]);
-      if (NI > 1) load_w(1, wf[1], sw[1]);
+      load_a(0, bfr[0]);
+      if (MJ > 1) load_a(1, bfr[1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        if (i + 2 < NI) load_w(i + 2, wf[(i + 2) % 3], sw[(i + 2) % 3]);
+      for (int j = 0; j < MJ; ++j) {
+        mfma(0, j);
+        later_read(j);
+        if (j == MJ - 1) {
 #pragma unroll
-        for (int j = 0; j < MJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              wf[i % 3], bfr[j], acc[i][j], kFmtW, 0, 0, sw[i % 3], 0, sab[j]);
+          for (int q = MJ; q < NA + NW; ++q) later_read(q);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // Instruction order for the scheduler (it otherwise hoists every weight read to
-      // the top and issues the MFMAs in bursts behind them): the slice's first reads,
-      // then each MFMA followed by one read of the fragment two steps ahead.
-      {
-        constexpr int kWReads =
-            (Lay::FP4W ? 1 : 2) + ((Lay::FP4W || GRAN == kSfbChannel) ? 1 : 0);
-        constexpr int kPro = 3 * MJ + (GRAN == kSfbBlock ? 1 : 0) + (NI > 1 ? 2 : 1) * kWReads;
-        __builtin_amdgcn_sched_group_barrier(0x100, kPro, 0);  // LDS reads
 #pragma unroll
-        for (int i = 0; i < NI; ++i)
+      for (int i = 1; i < NI; ++i) {
 #pragma unroll
-          for (int j = 0; j < MJ; ++j) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            if (i + 2 < NI && j < kWReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
+        for (int j = 0; j < MJ; ++j) {
+          mfma(i, j);
+          if (j == 0 && i + 2 < NI) load_w(i + 2, wf[(i + 2) % 3], sw[(i + 2) % 3]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     } else if constexpr (FP8) {
-      v8i bfr[MJ];
+      // Scales first: they are small reads, and the waits for them then never wait on
+      // the fragment reads issued behind them.
       float sa[MJ];
       const long oa = t.sfa_off + (long)s * t.sfa_ld + t.m0;
 #pragma unroll
       for (int j = 0; j < MJ; ++j) {
         const int row = wm0 + 16 * j + lr;
-        const uint8_t* rp = st + Lay::A_OFF + row * kSliceBytes;
-        const v4i lo = *reinterpret_cast<const v4i*>(rp + x_lo);
-        const v4i hi = *reinterpret_cast<const v4i*>(rp + x_hi);
-        bfr[j] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         if constexpr (SF == kSfF32)
           sa[j] = reinterpret_cast<const float*>(st + Lay::SA_OFF)[row];
         else
@@ -757,6 +766,13 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
           sbw = ue8m0_to_float(st[Lay::SB_OFF + 4 * lb + (int)(ob & 3)]);
         }
       }
+      // Activation fragment j: 16 rows x 128 K of the wave's rows.
+      auto load_a = [&](int j, v8i& b) {
+        const uint8_t* rp = st + Lay::A_OFF + (wm0 + 16 * j + lr) * kSliceBytes;
+        const v4i lo = *reinterpret_cast<const v4i*>(rp + x_lo);
+        const v4i hi = *reinterpret_cast<const v4i*>(rp + x_hi);
+        b = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      };
       // Weight fragment i (and its per-channel scales) from LDS.
       auto load_w = [&](int i, v8i& afr, v4f& sbv) {
         const uint8_t* rp = st + Lay::B_OFF + (wn0 + 16 * i + lr) * kSliceBytes;
@@ -780,56 +796,62 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
           }
         }
       };
-      // Software pipeline over the weight fragments: fragment i + 2 is read from LDS
-      // while the MJ partial sums of fragment i + 1 are issued and fragment i is
-      // promoted, so consecutive MFMAs are independent, the promotion FMAs overlap
-      // them and LDS latency stays off the critical path (format 0 = FP8 E4M3 for both
+      // Software pipeline, with its order fixed by scheduling fences (left alone, the
+      // scheduler waits for every read of the slice before the first MFMA and gathers
+      // most promotion FMAs behind the last one, where they cannot overlap MFMA work):
+      //  - the first MFMA waits only for weight fragment 0 and activation fragment 0;
+      //    each MFMA of weight fragment 0 is followed by one read of a later fragment;
+      //  - each MFMA of weight fragment i >= 1 is followed by the promotion of one
+      //    partial sum of fragment i - 1 into the float32 accumulator, so the FMAs run
+      //    while the MFMA pipe is busy; fragment i + 2 is read behind the last of them.
+      // Partial sums alternate between two register sets (format 0 = FP8 E4M3 for both
       // operands; scale exponent 127 = 2^0).
       const v4f zero = {0.f, 0.f, 0.f, 0.f};
       v4f part[2][MJ];
+      v8i bfr[MJ];
       v8i wf[3];
       v4f sv[3];
-      load_w(0, wf[0], sv[0]);
-      if (NI > 1) load_w(1, wf[1], sv[1]);
+      auto promote = [&](int i, int j) {
 #pragma unroll
-      for (int j = 0; j < MJ; ++j)
+        for (int r = 0; r < 4; ++r)
+          acc[i][j][r] = __builtin_fmaf(part[i & 1][j][r], sa[j] * sv[i % 3][r], acc[i][j][r]);
+      };
+      constexpr int NA = MJ > 2 ? MJ - 2 : 0;  // activation reads behind the first group
+      constexpr int NW = NI - 1 < 2 ? NI - 1 : 2;  // weight reads behind it
+      auto later_read = [&](int q) {
+        if (q < NA) load_a(q + 2, bfr[q + 2]);
+        else if (q - NA < NW) load_w(q - NA + 1, wf[q - NA + 1], sv[q - NA + 1]);
+      };
+      load_w(0, wf[0], sv[0]);
+      load_a(0, bfr[0]);
+      if (MJ > 1) load_a(1, bfr[1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < MJ; ++j) {
         part[0][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[0], bfr[j], zero, 0, 0,
                                                                       0, 127, 0, 127);
+        later_read(j);
+        if (j == MJ - 1) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        if (i + 2 < NI) load_w(i + 2, wf[(i + 2) % 3], sv[(i + 2) % 3]);
-        if (i + 1 < NI) {
-#pragma unroll
-          for (int j = 0; j < MJ; ++j)
-            part[(i + 1) & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                wf[(i + 1) % 3], bfr[j], zero, 0, 0, 0, 127, 0, 127);
+          for (int q = MJ; q < NA + NW; ++q) later_read(q);
         }
-#pragma unroll
-        for (int j = 0; j < MJ; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc[i][j][r] =
-                __builtin_fmaf(part[i & 1][j][r], sa[j] * sv[i % 3][r], acc[i][j][r]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // Instruction order for the scheduler: the slice's first reads and MFMAs, then
-      // each MFMA of fragment i + 1 followed by the promotion of one partial of fragment
-      // i and one read of fragment i + 2 (left alone, the scheduler places each
-      // promotion right behind the MFMA that produces it and stalls on it).
-      {
-        constexpr int kWReads = 2 + (GRAN == kSfbChannel ? 1 : 0);
-        constexpr int kPro = 3 * MJ + (GRAN == kSfbBlock ? 1 : 0) + (NI > 1 ? 2 : 1) * kWReads;
-        constexpr int kVal = GRAN == kSfbChannel ? 8 : 4;
-        __builtin_amdgcn_sched_group_barrier(0x100, kPro, 0);  // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, MJ, 0);    // MFMAs of fragment 0
 #pragma unroll
-        for (int i = 0; i < NI; ++i)
+      for (int i = 1; i < NI; ++i) {
 #pragma unroll
-          for (int j = 0; j < MJ; ++j) {
-            if (i + 1 < NI) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, kVal, 0);  // VALU
-            if (i + 2 < NI && j < kWReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
+        for (int j = 0; j < MJ; ++j) {
+          part[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              wf[i % 3], bfr[j], zero, 0, 0, 0, 127, 0, 127);
+          promote(i - 1, j);
+          // fragment i + 2 reuses the registers of fragment i - 1, whose scales the
+          // promotions above still read
+          if (j == MJ - 1 && i + 2 < NI) load_w(i + 2, wf[(i + 2) % 3], sv[(i + 2) % 3]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+#pragma unroll
+      for (int j = 0; j < MJ; ++j) promote(NI - 1, j);
     } else {
       // 32x32x16 MFMAs: MFMA h of the slice takes K elements 16h .. 16h + 15; lane group
       // g = lane / 32 supplies elements 16h + 8g .. 16h + 8g + 7, the 16-byte chunk
@@ -965,7 +987,7 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
             const v4f x = acc[2 * h][j], y = acc[2 * h + 1][j];
             const v4i w = {(int)pack_bf16x2(x[0], x[1]), (int)pack_bf16x2(x[2], x[3]),
                            (int)pack_bf16x2(y[0], y[1]), (int)pack_bf16x2(y[2], y[3])};
-            const bool ok = row_ok && n_start + 8 * h + 8 <= p.N;
+            const bool ok = row_ok && n_start + 8 * h + 8 <= t.n_end;
             const uint32_t voff = ok ? (uint32_t)(((long)rl * p.N + n_start + 8 * h) * 2) : kOOB;
             store_b128(rs_d, voff, w);
           }
@@ -1008,7 +1030,7 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
                              (int)pack_bf16x2(v[8 * h + 2], v[8 * h + 3]),
                              (int)pack_bf16x2(v[8 * h + 4], v[8 * h + 5]),
                              (int)pack_bf16x2(v[8 * h + 6], v[8 * h + 7])};
-              const bool ok = row_ok && n_start + 8 * h + 8 <= p.N;
+              const bool ok = row_ok && n_start + 8 * h + 8 <= t.n_end;
               const uint32_t voff = ok ? (uint32_t)(((long)rl * p.N + n_start + 8 * h) * 2) : kOOB;
               store_b128(rs_d, voff, w);
             }
@@ -1088,7 +1110,9 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
           for (int j = 0; j < MJ2; ++j) acc2[i][j] = (v16f){};
       }
     }
-    compute(tc, sc, stg);
+    // a wave whose columns all lie beyond N (the last n-tile of a ragged N) has nothing
+    // to compute; its stores are all masked
+    if (ACC || wn0 < tc.n_end - tc.n0) compute(tc, sc, stg);
     const bool epi = sc == tc.nk - 1;
     if (epi) {
       epilogue(tc, stg, rx);
