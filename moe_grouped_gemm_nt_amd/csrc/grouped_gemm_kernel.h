@@ -251,6 +251,8 @@ __device__ __forceinline__ long first_tile() {
 
 // Decodes logical tile L; tiles with nothing to do are skipped by advancing L in steps
 // of the grid size, and L is left at the tile returned.
+constexpr int kKGroupM = 8;  // K-grouped tile order: m-tiles per group (see decode_tile)
+
 template <class T, int VAR, int DT, int GRAN>
 __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Params& p, long& L) {
   TileCtx t = {};  // valid == 0, null bases: an idle cursor copies nothing
@@ -359,11 +361,15 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       const int se = __builtin_amdgcn_readfirstlane(S.s_a[e]);
       const int k = (__builtin_amdgcn_readfirstlane(S.s_a[e + 1]) & ~kKUnusable) - se;
       if ((se & kKUnusable) || (k == 0 && p.accumulate)) { L += gridDim.x; continue; }
-      // n-tile fastest: the tiles an XCD runs at once cover whole output rows, so the
-      // accumulation input and output stream through long contiguous runs (measured 2 %
-      // faster than m-tile fastest on the weight-gradient shape; the operands are small
-      // enough to stay in L2 either way)
-      const int mt = local / S.ntn, nt = local % S.ntn;
+      // Tiles go in groups of kKGroupM m-tiles, m-tile fastest inside a group, so the 32
+      // tiles an XCD runs at once cover 8 m-tiles x 4 n-tiles of the output: each XCD
+      // then reads a quarter of the expert's N-side operand per round instead of all of it
+      // (with n-tile fastest every XCD read the whole N-side operand: 8x its bytes).
+      const int gm = local / (kKGroupM * S.ntn);        // group of kKGroupM m-tiles
+      const int m_first = gm * kKGroupM;
+      const int gsz = min(kKGroupM, S.mtn - m_first);   // m-tiles in this group
+      const int in_g = local - gm * kKGroupM * S.ntn;
+      const int mt = m_first + in_g % gsz, nt = in_g / gsz;
       const long pe = se;
       t.valid = 1;
       t.g = e;
