@@ -444,7 +444,8 @@ def quant_bench(dev, args):
             t = time.perf_counter() - w0
         cpu = {"value": round(rows * abytes / M * passes / t / 1e9, 4), "unit": "GB/s",
                "cores": 1, "kind": "oracle",
-               "sample": f"{rows} rows x {in_cols} per pass; {passes} passes in {t:.1f} s"}
+               "sample": f"{rows} rows x {in_cols} per pass; {passes} passes in {t:.1f} s",
+               "cpu": host_cpu_model()}
     what = "SwiGLU + FP8 1x128 re-quantization" if swiglu else "FP8 1x128 activation quantization"
     line = {
         "metric": f"{what} throughput (algorithmic bytes)",
@@ -666,6 +667,18 @@ def summarize(args):
         print(f"wrote {path}")
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name (first entry of /proc/cpuinfo), for the baseline record."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(p, opt, flops, target_s):
     """The oracle, as it stands, on the host cores: a bounded sample of the same workload
     (whole experts, or a subset of experts for the large masked shapes)."""
@@ -726,7 +739,8 @@ def cpu_baseline(p, opt, flops, target_s):
             break
     return {"value": round(unit_flops * passes / t / 1e12, 6), "unit": "TFLOPS",
             "cores": int(threads), "kind": "oracle",
-            "sample": f"{sample}; {passes} passes in {t:.1f} s (FP64 numpy/BLAS)"}
+            "sample": f"{sample}; {passes} passes in {t:.1f} s (FP64 numpy/BLAS)",
+            "cpu": host_cpu_model()}
 
 
 if __name__ == "__main__":

@@ -133,3 +133,9 @@ def test_traffic_only_for_the_current_kernel_sources(tmp_path, monkeypatch, work
     # the two kernels are built from different sources, so their digests differ
     assert bench.kernel_source_digest(bench.KERNEL_NAME) != \
         bench.kernel_source_digest(bench.QUANT_KERNEL_NAME)
+
+
+def test_host_cpu_model_is_named():
+    """The oracle baseline names the host CPU it ran on."""
+    name = bench.host_cpu_model()
+    assert isinstance(name, str) and name
