@@ -361,10 +361,11 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       const int se = __builtin_amdgcn_readfirstlane(S.s_a[e]);
       const int k = (__builtin_amdgcn_readfirstlane(S.s_a[e + 1]) & ~kKUnusable) - se;
       if ((se & kKUnusable) || (k == 0 && p.accumulate)) { L += gridDim.x; continue; }
-      // Tiles go in groups of kKGroupM m-tiles, m-tile fastest inside a group, so the 32
-      // tiles an XCD runs at once cover 8 m-tiles x 4 n-tiles of the output: each XCD
-      // then reads a quarter of the expert's N-side operand per round instead of all of it
-      // (with n-tile fastest every XCD read the whole N-side operand: 8x its bytes).
+      // Tiles go in groups of kKGroupM m-tiles, m-tile fastest inside a group. With a
+      // 256-workgroup grid each XCD runs 32 consecutive tiles at once, which then cover
+      // 8 m-tiles x 4 n-tiles of the output: each XCD reads a quarter of the expert's N-side
+      // operand per round instead of all of it (with n-tile fastest every XCD read the
+      // whole N-side operand: 8x its bytes). Any grid gives the same results.
       const int gm = local / (kKGroupM * S.ntn);        // group of kKGroupM m-tiles
       const int m_first = gm * kKGroupM;
       const int gsz = min(kKGroupM, S.mtn - m_first);   // m-tiles in this group
