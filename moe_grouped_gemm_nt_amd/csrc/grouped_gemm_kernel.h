@@ -61,9 +61,11 @@ struct Sched {
   int* s_b;    // masked, psum: row counts [G]; contiguous: packed (block << 12 | expert)
                // of each valid block
   int* s_c;    // psum: first row of each expert's segment [G]
-  int total;   // number of tiles
+  int total;   // number of tiles (a split last round counts each piece)
   int ntn;     // n tiles per expert
   int mtn;     // K-grouped: m tiles per expert
+  int split_base;  // M-grouped: first tile of a last round that is split along N
+  int split_p;     // pieces per tile of that round (1: no split)
 };
 
 // LDS layout of one pipeline stage. Every region is a whole number of copy
@@ -132,6 +134,29 @@ struct Layout {
   static_assert(!(ACC && VAR != kKGrouped), "accumulation is K-grouped only");
 };
 
+// The tiles of an M-grouped call go in rounds of one per workgroup. When there are at
+// least two rounds and the last would leave at least half of the workgroups idle, each of
+// its tiles is split along N into 2 or 4 pieces of whole wave columns, one per
+// workgroup: every output is computed exactly as in the whole tile, and a memory-bound
+// last round gets two or four times as many CUs fetching its weights.
+template <class T, int VAR>
+__device__ __forceinline__ void split_last_round(Sched<T, VAR>& S) {
+  S.split_base = S.total;
+  S.split_p = 1;
+  const int grid = gridDim.x;
+  if (S.total <= grid) return;
+  const int base = (S.total - 1) / grid * grid;  // first tile of the last round
+  const int last = S.total - base;
+  int pieces = 1;
+  if (4 * last <= grid && T::BN / 4 >= T::WTN) pieces = 4;
+  else if (2 * last <= grid && T::BN / 2 >= T::WTN) pieces = 2;
+  if (pieces > 1) {
+    S.split_base = base;
+    S.split_p = pieces;
+    S.total = base + last * pieces;
+  }
+}
+
 template <class T, int VAR, int NT>
 __device__ __forceinline__ void sched_init(Sched<T, VAR>& S, const Params& p, int* s_tmp,
                                            int* s_flag) {
@@ -146,6 +171,7 @@ __device__ __forceinline__ void sched_init(Sched<T, VAR>& S, const Params& p, in
     }
     __syncthreads();
     S.total = block_exclusive_scan<NT>(S.s_a, p.G, s_tmp);
+    split_last_round(S);
   } else if constexpr (VAR == kPsum) {
     // Expert g owns rows [start_g, end_g): end_g = clamp(psum[g], 0, M) raised to the
     // running maximum of the earlier ends, start_g = end_{g-1} (0 for g = 0), so the
@@ -178,6 +204,7 @@ __device__ __forceinline__ void sched_init(Sched<T, VAR>& S, const Params& p, in
     }
     __syncthreads();
     S.total = block_exclusive_scan<NT>(S.s_a, p.G, s_tmp);
+    split_last_round(S);
   } else if constexpr (VAR == kContig) {
     // s_flag (transient, inside the pipeline stages) holds the block flags and then
     // their prefix; s_ent (transient, after it) the block's packed entry. Valid blocks are
@@ -207,6 +234,10 @@ __device__ __forceinline__ void sched_init(Sched<T, VAR>& S, const Params& p, in
       if (s_ent[b] >> 24) S.s_b[s_flag[b]] = s_ent[b];
     __syncthreads();
     S.total = nvalid * SUB * S.ntn;
+    S.split_base = S.total;
+    S.split_p = 1;
+    // 128-row tiles only: every logical tile is then a real one (no padding sub-tiles)
+    if constexpr (SUB == 1 && !T::SWI) split_last_round(S);
   } else {
     // p_e = sum_{j<e} max(k_j, 0) saturated at K + 1: an expert is usable only if its
     // tokens end at or before K, so the saturation changes no decision, and no routing
@@ -235,6 +266,8 @@ __device__ __forceinline__ void sched_init(Sched<T, VAR>& S, const Params& p, in
     }
     __syncthreads();
     S.total = p.G * S.mtn * S.ntn;
+    S.split_base = S.total;
+    S.split_p = 1;
   }
 }
 
@@ -259,23 +292,33 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
   constexpr int esz = DT == kBF16 ? 2 : 1;  // activation bytes per element
   if constexpr (VAR == kMasked || VAR == kPsum) {
     if (L < S.total) {
-      int lo = 0, hi = p.G - 1;  // largest g with prefix[g] <= L
+      long Lt = L;  // the tile (of which L is one piece in a split last round)
+      int piece = 0, pieces = 1;
+      if (L >= S.split_base) {
+        pieces = S.split_p;
+        Lt = S.split_base + (L - S.split_base) / pieces;
+        piece = (int)((L - S.split_base) % pieces);
+      }
+      int lo = 0, hi = p.G - 1;  // largest g with prefix[g] <= Lt
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (S.s_a[mid] <= L) lo = mid; else hi = mid - 1;
+        if (S.s_a[mid] <= Lt) lo = mid; else hi = mid - 1;
       }
       const int g = lo;
       const int c = S.s_b[g];
       const int mt_g = (c + T::BM - 1) / T::BM;
-      const int local = (int)(L - S.s_a[g]);
+      const int local = (int)(Lt - S.s_a[g]);
       const int nt = local / mt_g, mt = local % mt_g;
       const int Kb = p.K * esz;
       const int KB = p.K / 128;
       t.valid = 1;
       t.g = g;
       t.m0 = mt * T::BM;
-      t.n0 = nt * T::BN;
-      t.n_end = T::SWI ? p.N : min(p.N, t.n0 + T::BN);
+      // a piece of the last, ragged n-tile may start at or past N: it is then empty
+      // (n_end == n0), its weight resource has size 0 and it stores nothing
+      const int width = T::BN / pieces;
+      t.n0 = nt * T::BN + piece * width;
+      t.n_end = T::SWI ? p.N : max(t.n0, min(p.N, t.n0 + width));
       t.k_bytes = Kb;
       t.nk = (Kb + kSliceBytes - 1) / kSliceBytes;
       t.a_lim = c;
@@ -309,8 +352,15 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
   } else if constexpr (VAR == kContig) {
     constexpr int SUB = kContigBlock / T::BM;
     while (L < S.total) {
-      const int nt = (int)(L % S.ntn);
-      const long rest = L / S.ntn;
+      long Lt = L;  // the tile (of which L is one piece in a split last round)
+      int piece = 0, pieces = 1;
+      if (L >= S.split_base) {
+        pieces = S.split_p;
+        Lt = S.split_base + (L - S.split_base) / pieces;
+        piece = (int)((L - S.split_base) % pieces);
+      }
+      const int nt = (int)(Lt % S.ntn);
+      const long rest = Lt / S.ntn;
       const int sub = (int)(rest % SUB);
       const int packed = S.s_b[rest / SUB];
       const int blk = (packed >> 12) & 0xfff, e = packed & 0xfff, nsub = packed >> 24;
@@ -323,8 +373,9 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       t.valid = 1;
       t.g = e;
       t.m0 = m0;
-      t.n0 = nt * T::BN;
-      t.n_end = T::SWI ? p.N : min(p.N, t.n0 + T::BN);
+      const int width = T::BN / pieces;
+      t.n0 = nt * T::BN + piece * width;
+      t.n_end = T::SWI ? p.N : max(t.n0, min(p.N, t.n0 + width));
       t.k_bytes = Kb;
       t.nk = (Kb + kSliceBytes - 1) / kSliceBytes;
       t.a_lim = p.rows;
@@ -335,7 +386,7 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       t.a_bytes = (uint32_t)(rt * Kb);
       t.b_row0 = T::SWI ? 0 : t.n0;
       t.b_base = p.B + ((long)e * p.N + t.b_row0) * Kbw;
-      t.b_bytes = (uint32_t)((T::SWI ? (long)p.N : min((long)T::BN, (long)(p.N - t.n0))) * Kbw);
+      t.b_bytes = (uint32_t)((T::SWI ? (long)p.N : (long)(t.n_end - t.n0)) * Kbw);
       t.lda = Kb;
       t.ldb = Kbw;
       t.sfa_off = 0;

@@ -384,3 +384,45 @@ def test_kgrouped_routing_beyond_int32(mode):
         if not want[e]:
             assert torch.equal(D[e], C[e]), f"expert {e} must be left untouched"
     assert_report(rep, "fp8")
+
+
+# ----------------------------------------------------------------------------- split last round
+# 100 experts (or row blocks) of one 128-row tile each x 3 n-tiles of the 128 x 256 tile =
+# 300 tiles: one full round of 256 workgroups and a last round of 44 tiles, which the
+# scheduler splits along N (FP8: four pieces of 64 columns, BF16: two of 128). N = 520 makes
+# the last n-tile ragged, so pieces of it start past N and must stay empty. Every output is
+# checked against the oracle and bitwise against the 32-row tile, which does not split.
+
+
+@pytest.mark.parametrize("variant", ["masked", "contiguous", "psum"])
+@pytest.mark.parametrize("dtype,sf_fmt,gran", [
+    ("fp8", "f32", "block128"),
+    ("fp8", "ue8m0", "channel"),
+    ("bf16", "f32", "block128"),
+])
+def test_split_last_round_ragged_n(variant, dtype, sf_fmt, gran):
+    G, N, K = 100, 520, 256
+    rng = np.random.default_rng(61)
+    segs = rng.integers(1, 129, size=G)
+    segs[[0, G - 1]] = [128, 1]
+    say("split last round", variant, dtype, sf_fmt, gran)
+    if variant == "masked":
+        p = synth.make_masked(dtype, G, 128, N, K, segs, seed=61, device=DEV, sf_fmt=sf_fmt,
+                              sfb_gran=gran)
+        run, check = run_masked, check_masked
+    elif variant == "contiguous":
+        p = synth.make_contiguous(dtype, G, N, K, segs, seed=61, device=DEV, sf_fmt=sf_fmt,
+                                  sfb_gran=gran, M_max=128 * G)
+        run, check = run_contiguous, check_contiguous
+    else:
+        p = synth.make_contiguous_psum(dtype, G, N, K, segs, seed=61, device=DEV,
+                                       sf_fmt=sf_fmt, sfb_gran=gran, tail=3)
+        run, check = run_psum, check_psum
+    outs = []
+    for em in (16, 100):  # the 32-row tile, then the 128 x 256 tile
+        say("  expected_m", em)
+        D = run(p, em)
+        torch.cuda.synchronize()
+        outs.append(bf16_bits(D))
+    assert_report(check(p, D), dtype)
+    assert (outs[0] == outs[1]).all(), "the split tile disagrees with the 32-row tile"
