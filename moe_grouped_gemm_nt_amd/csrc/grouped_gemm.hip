@@ -41,6 +41,10 @@ using TileL = Tile<128, 256, 2, 2, 3>;   // larger experts, BF16
 // the K = 256 contiguous shape, whose tiles are mostly epilogue, and 2-4 % on the
 // MFMA-bound 6 x 4096 x 4096 shape; BF16 is better served by four)
 using TileL8 = Tile<128, 256, 2, 4, 3>;
+// ... except masked FP8 calls with 129-256 rows per expert (two m-tiles, the second partly
+// padding, and a weight stream that sets the time): there four MFMA waves of 64 x 128 (the
+// BF16 tile's shape) measured 3 % faster on the 32-expert N = 6144, K = 7168 shape, and
+// 3-6 % slower on the 6-expert, FP4-weight and contiguous shapes (interleaved A/B runs)
 // the fused SwiGLU tile: 128 output columns (their gate and up weight rows), eight waves
 // of 16 rows x all 256 weight rows; the two-stage form takes over when the row-block table
 // of a long contiguous layout (beyond ~2900 blocks) no longer fits next to three stages
@@ -48,7 +52,7 @@ using TileSwi = Tile<128, 256, 8, 1, 3, true>;
 using TileSwi2 = Tile<128, 256, 8, 1, 2, true>;
 using TileK = Tile<64, 128, 2, 2, 3>;    // K-grouped output tiles
 
-enum TileId { kTileS = 0, kTileM = 1, kTileL = 2 };
+enum TileId { kTileS = 0, kTileM = 1, kTileL = 2, kTileL4 = 3 };
 
 struct DevInfo {
   int id = 0;
@@ -157,6 +161,11 @@ long m_tiles(const Params& p) {
 
 template <int VAR, int DT, int SF, int GRAN>
 mgg_status launch_tile(TileId tile, const Params& p, hipStream_t s) {
+  if constexpr (VAR == kMasked && DT == kFP8) {
+    if (tile == kTileL4 && lds_bytes<TileL, VAR, DT, SF, GRAN, false>(p) <= kLdsBytes)
+      return launch<TileL, VAR, DT, SF, GRAN, false>(p, m_tiles<TileL, VAR>(p), s);
+  }
+  if (tile == kTileL4) tile = kTileL;
   // The largest tile needs the most LDS; fall back to the middle one when the
   // scheduler table does not fit next to it.
   using TileLg = std::conditional_t<DT == kBF16, TileL, TileL8>;
@@ -344,7 +353,9 @@ mgg_status grouped_gemm_masked(mgg_dtype dt, int G, int cap, int N, int K, const
   p.sfa_bytes = dt != MGG_BF16 ? scale_bytes(sfa_n, sf) : 0;
   p.sfb_bytes = dt != MGG_BF16 ? scale_bytes(sfb_n, sf) : 0;
   p.meta_bytes = (uint32_t)G * 4;
-  return dispatch_m<kMasked>(dt, sf, gran, pick_tile(expected_m, cap), p, stream);
+  TileId tile = pick_tile(expected_m, cap);
+  if (tile == kTileL && expected_m > 128 && expected_m <= 256) tile = kTileL4;
+  return dispatch_m<kMasked>(dt, sf, gran, tile, p, stream);
 }
 
 mgg_status grouped_gemm_contiguous(mgg_dtype dt, int G, int M, int N, int K, const void* A,
