@@ -47,7 +47,8 @@ KERNEL_NAME = "grouped_gemm_kernel"
 QUANT_KERNEL_NAME = "quant_rows_1x128"
 # the sources each kernel is compiled from (the public header only declares entry points)
 KERNEL_SOURCES = {
-    KERNEL_NAME: ("gemm_engine.h", "grouped_gemm_kernel.h", "grouped_gemm.hip", "act_math.h"),
+    KERNEL_NAME: ("gemm_engine.h", "grouped_gemm_kernel.h", "tile_map.h", "grouped_gemm.hip",
+                  "act_math.h"),
     QUANT_KERNEL_NAME: ("quantize.hip", "act_math.h"),
 }
 

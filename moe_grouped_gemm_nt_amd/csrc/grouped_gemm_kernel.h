@@ -27,6 +27,7 @@
 
 #include "act_math.h"
 #include "gemm_engine.h"
+#include "tile_map.h"
 
 namespace mgg {
 
@@ -134,27 +135,16 @@ struct Layout {
   static_assert(!(ACC && VAR != kKGrouped), "accumulation is K-grouped only");
 };
 
-// The tiles of an M-grouped call go in rounds of one per workgroup. When there are at
-// least two rounds and the last would leave at least half of the workgroups idle, each of
-// its tiles is split along N into 2 or 4 pieces of whole wave columns, one per
-// workgroup: every output is computed exactly as in the whole tile, and a memory-bound
-// last round gets two or four times as many CUs fetching its weights.
+// The tiles of an M-grouped call go in rounds of one per workgroup; a mostly idle last
+// round is split along N (split_last_round in tile_map.h): every output is computed
+// exactly as in the whole tile, and a memory-bound last round gets two or four times as
+// many CUs fetching its weights.
 template <class T, int VAR>
-__device__ __forceinline__ void split_last_round(Sched<T, VAR>& S) {
-  S.split_base = S.total;
-  S.split_p = 1;
-  const int grid = gridDim.x;
-  if (S.total <= grid) return;
-  const int base = (S.total - 1) / grid * grid;  // first tile of the last round
-  const int last = S.total - base;
-  int pieces = 1;
-  if (4 * last <= grid && T::BN / 4 >= T::WTN) pieces = 4;
-  else if (2 * last <= grid && T::BN / 2 >= T::WTN) pieces = 2;
-  if (pieces > 1) {
-    S.split_base = base;
-    S.split_p = pieces;
-    S.total = base + last * pieces;
-  }
+__device__ __forceinline__ void split_rounds(Sched<T, VAR>& S) {
+  const SplitRound r = split_last_round(S.total, gridDim.x, T::BN, T::WTN);
+  S.split_base = r.base;
+  S.split_p = r.pieces;
+  S.total = r.total;
 }
 
 template <class T, int VAR, int NT>
@@ -171,7 +161,7 @@ __device__ __forceinline__ void sched_init(Sched<T, VAR>& S, const Params& p, in
     }
     __syncthreads();
     S.total = block_exclusive_scan<NT>(S.s_a, p.G, s_tmp);
-    split_last_round(S);
+    split_rounds(S);
   } else if constexpr (VAR == kPsum) {
     // Expert g owns rows [start_g, end_g): end_g = clamp(psum[g], 0, M) raised to the
     // running maximum of the earlier ends, start_g = end_{g-1} (0 for g = 0), so the
@@ -204,7 +194,7 @@ __device__ __forceinline__ void sched_init(Sched<T, VAR>& S, const Params& p, in
     }
     __syncthreads();
     S.total = block_exclusive_scan<NT>(S.s_a, p.G, s_tmp);
-    split_last_round(S);
+    split_rounds(S);
   } else if constexpr (VAR == kContig) {
     // s_flag (transient, inside the pipeline stages) holds the block flags and then
     // their prefix; s_ent (transient, after it) the block's packed entry. Valid blocks are
@@ -237,7 +227,7 @@ __device__ __forceinline__ void sched_init(Sched<T, VAR>& S, const Params& p, in
     S.split_base = S.total;
     S.split_p = 1;
     // 128-row tiles only: every logical tile is then a real one (no padding sub-tiles)
-    if constexpr (SUB == 1 && !T::SWI) split_last_round(S);
+    if constexpr (SUB == 1 && !T::SWI) split_rounds(S);
   } else {
     // p_e = sum_{j<e} max(k_j, 0) saturated at K + 1: an expert is usable only if its
     // tokens end at or before K, so the saturation changes no decision, and no routing
@@ -272,14 +262,9 @@ __device__ __forceinline__ void sched_init(Sched<T, VAR>& S, const Params& p, in
 }
 
 // Logical index of the workgroup's first tile; its later tiles follow in steps of the
-// grid size. Workgroups are dispatched to the 8 XCDs round-robin (block b runs on XCD
-// b % 8); each XCD gets a contiguous range of logical tiles per round so that
-// neighbouring tiles (same expert, same weight panel) share that XCD's L2.
+// grid size (the XCD-aware order of first_tile_of in tile_map.h).
 __device__ __forceinline__ long first_tile() {
-  const int grid = gridDim.x, b = blockIdx.x;
-  if (grid % kXcds != 0) return b;
-  const int per = grid / kXcds;
-  return (long)(b % kXcds) * per + b / kXcds;
+  return first_tile_of(blockIdx.x, gridDim.x, kXcds);
 }
 
 // Decodes logical tile L; tiles with nothing to do are skipped by advancing L in steps
@@ -292,33 +277,19 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
   constexpr int esz = DT == kBF16 ? 2 : 1;  // activation bytes per element
   if constexpr (VAR == kMasked || VAR == kPsum) {
     if (L < S.total) {
-      long Lt = L;  // the tile (of which L is one piece in a split last round)
-      int piece = 0, pieces = 1;
-      if (L >= S.split_base) {
-        pieces = S.split_p;
-        Lt = S.split_base + (L - S.split_base) / pieces;
-        piece = (int)((L - S.split_base) % pieces);
-      }
-      int lo = 0, hi = p.G - 1;  // largest g with prefix[g] <= Lt
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (S.s_a[mid] <= Lt) lo = mid; else hi = mid - 1;
-      }
-      const int g = lo;
+      const Piece q = piece_of(L, S.split_base, S.split_p);
+      const int g = expert_of_tile(q.tile, S.s_a, p.G);
       const int c = S.s_b[g];
       const int mt_g = (c + T::BM - 1) / T::BM;
-      const int local = (int)(Lt - S.s_a[g]);
-      const int nt = local / mt_g, mt = local % mt_g;
+      int mt, nt;
+      expert_tile((int)(q.tile - S.s_a[g]), mt_g, &mt, &nt);
       const int Kb = p.K * esz;
       const int KB = p.K / 128;
       t.valid = 1;
       t.g = g;
       t.m0 = mt * T::BM;
-      // a piece of the last, ragged n-tile may start at or past N: it is then empty
-      // (n_end == n0), its weight resource has size 0 and it stores nothing
-      const int width = T::BN / pieces;
-      t.n0 = nt * T::BN + piece * width;
-      t.n_end = T::SWI ? p.N : max(t.n0, min(p.N, t.n0 + width));
+      // an empty piece (n_end == n0) has a weight resource of size 0 and stores nothing
+      piece_columns(nt, T::BN, q.piece, q.pieces, p.N, &t.n0, &t.n_end);
       t.k_bytes = Kb;
       t.nk = (Kb + kSliceBytes - 1) / kSliceBytes;
       t.a_lim = c;
@@ -352,17 +323,10 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
   } else if constexpr (VAR == kContig) {
     constexpr int SUB = kContigBlock / T::BM;
     while (L < S.total) {
-      long Lt = L;  // the tile (of which L is one piece in a split last round)
-      int piece = 0, pieces = 1;
-      if (L >= S.split_base) {
-        pieces = S.split_p;
-        Lt = S.split_base + (L - S.split_base) / pieces;
-        piece = (int)((L - S.split_base) % pieces);
-      }
-      const int nt = (int)(Lt % S.ntn);
-      const long rest = Lt / S.ntn;
-      const int sub = (int)(rest % SUB);
-      const int packed = S.s_b[rest / SUB];
+      const Piece q = piece_of(L, S.split_base, S.split_p);
+      int block, sub, nt;
+      contiguous_tile(q.tile, S.ntn, SUB, &block, &sub, &nt);
+      const int packed = S.s_b[block];
       const int blk = (packed >> 12) & 0xfff, e = packed & 0xfff, nsub = packed >> 24;
       const int m0 = blk * kContigBlock + sub * T::BM;
       // A sub-tile that starts on padding is padding throughout (valid rows come first
@@ -373,9 +337,12 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       t.valid = 1;
       t.g = e;
       t.m0 = m0;
-      const int width = T::BN / pieces;
-      t.n0 = nt * T::BN + piece * width;
-      t.n_end = T::SWI ? p.N : max(t.n0, min(p.N, t.n0 + width));
+      if constexpr (T::SWI) {
+        t.n0 = nt * T::BN;
+        t.n_end = p.N;
+      } else {
+        piece_columns(nt, T::BN, q.piece, q.pieces, p.N, &t.n0, &t.n_end);
+      }
       t.k_bytes = Kb;
       t.nk = (Kb + kSliceBytes - 1) / kSliceBytes;
       t.a_lim = p.rows;
@@ -412,16 +379,10 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       const int se = __builtin_amdgcn_readfirstlane(S.s_a[e]);
       const int k = (__builtin_amdgcn_readfirstlane(S.s_a[e + 1]) & ~kKUnusable) - se;
       if ((se & kKUnusable) || (k == 0 && p.accumulate)) { L += gridDim.x; continue; }
-      // Tiles go in groups of kKGroupM m-tiles, m-tile fastest inside a group. With a
-      // 256-workgroup grid each XCD runs 32 consecutive tiles at once, which then cover
-      // 8 m-tiles x 4 n-tiles of the output: each XCD reads a quarter of the expert's N-side
-      // operand per round instead of all of it (with n-tile fastest every XCD read the
-      // whole N-side operand: 8x its bytes). Any grid gives the same results.
-      const int gm = local / (kKGroupM * S.ntn);        // group of kKGroupM m-tiles
-      const int m_first = gm * kKGroupM;
-      const int gsz = min(kKGroupM, S.mtn - m_first);   // m-tiles in this group
-      const int in_g = local - gm * kKGroupM * S.ntn;
-      const int mt = m_first + in_g % gsz, nt = in_g / gsz;
+      // groups of kKGroupM m-tiles (kgrouped_tile in tile_map.h): with n-tile fastest,
+      // every XCD read the expert's whole N-side operand in each round (8x its bytes)
+      int mt, nt;
+      kgrouped_tile(local, S.mtn, S.ntn, kKGroupM, &mt, &nt);
       const long pe = se;
       t.valid = 1;
       t.g = e;
