@@ -1129,9 +1129,10 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
           for (int j = 0; j < MJ2; ++j) acc2[i][j] = (v16f){};
       }
     }
-    // a wave whose columns all lie beyond N (the last n-tile of a ragged N) has nothing
-    // to compute; its stores are all masked
-    if (ACC || wn0 < tc.n_end - tc.n0) compute(tc, sc, stg);
+    // a wave whose columns all lie beyond N (the last n-tile of a ragged N) or whose rows
+    // all lie at or past the tile's valid rows (the padding of an expert's last m-tile)
+    // has nothing to compute: the epilogue stores none of its outputs
+    if (ACC || (wn0 < tc.n_end - tc.n0 && tc.m0 + wm0 < tc.row_end)) compute(tc, sc, stg);
     const bool epi = sc == tc.nk - 1;
     if (epi) {
       epilogue(tc, stg, rx);
