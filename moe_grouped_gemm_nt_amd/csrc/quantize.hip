@@ -75,6 +75,7 @@ __global__ __launch_bounds__(kThreadsQ) void quant_rows_1x128(const uint16_t* __
   const int rows_log = QS::kUnitsLog - gb_log;  // U / GB rows per block
   const int m0 = blockIdx.x << rows_log;
   const long ldx = SWIGLU ? 2L * K : (long)K;
+  // X is read once and Q written once: both go through the non-temporal cache policy
   u32x4 w[ST], u[ST];
   int rl[ST], kb[ST];
 #pragma unroll
@@ -87,8 +88,8 @@ __global__ __launch_bounds__(kThreadsQ) void quant_rows_1x128(const uint16_t* __
     w[r] = (u32x4){0u, 0u, 0u, 0u};
     u[r] = (u32x4){0u, 0u, 0u, 0u};
     if (m < M && kb[r] * 128 < K) {  // uniform per 16-lane quarter
-      w[r] = *reinterpret_cast<const u32x4*>(X + (long)m * ldx + col);
-      if constexpr (SWIGLU) u[r] = *reinterpret_cast<const u32x4*>(X + (long)m * ldx + K + col);
+      w[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(X + (long)m * ldx + col));
+      if constexpr (SWIGLU) u[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(X + (long)m * ldx + K + col));
     }
   }
 #pragma unroll
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(kThreadsQ) void quant_rows_1x128(const uint16_t* __
     u32x2 out;
     out.x = to_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
     out.y = to_e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
-    if (m < M && kb[r] * 128 < K) *reinterpret_cast<u32x2*>(Q + (long)m * K + col) = out;
+    if (m < M && kb[r] * 128 < K) __builtin_nontemporal_store(out, reinterpret_cast<u32x2*>(Q + (long)m * K + col));
     const int g = kb[r] - (blockIdx.y << gb_log);
     if (l16 == 0) s_sf[(g << rows_log) + rl[r]] = sfbits;
   }
