@@ -514,7 +514,9 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int cwave = (wave - Lay::COPY0) & 3;  // slot index of a copy wave
   const int lr = lane & 15, lg = lane >> 4;
-  const int wave_m = wave / T::WN, wave_n = wave % T::WN;
+  // MFMA waves are numbered down the tile's columns, so the waves of one wave column (all
+  // the work of a 64-column piece of a split last round) sit on different SIMDs
+  const int wave_m = wave % T::WM, wave_n = wave / T::WM;
   const int wm0 = wave_m * T::WTM, wn0 = wave_n * T::WTN;
 
   // ---- scheduler (its scan scratch lies in the pipeline stages, unused until the
