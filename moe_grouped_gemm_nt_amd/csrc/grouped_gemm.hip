@@ -167,8 +167,10 @@ mgg_status launch_tile(TileId tile, const Params& p, hipStream_t s) {
   }
   if (tile == kTileL4) tile = kTileL;
   // The largest tile needs the most LDS; fall back to the middle one when the
-  // scheduler table does not fit next to it.
-  using TileLg = std::conditional_t<DT == kBF16, TileL, TileL8>;
+  // scheduler table does not fit next to it. Contiguous FP8 calls with float32
+  // per-channel weight scales take the four-wave 128x256 tile: with eight waves they need
+  // more than the 168 registers three waves per SIMD leave.
+  using TileLg = std::conditional_t<DT == kBF16 || (VAR == kContig && DT == kFP8 && SF == kSfF32 && GRAN == kSfbChannel), TileL, TileL8>;
   if (tile == kTileL && lds_bytes<TileLg, VAR, DT, SF, GRAN, false>(p) > kLdsBytes) tile = kTileM;
   using TileS = std::conditional_t<DT == kBF16, TileS16, TileS8>;
   switch (tile) {

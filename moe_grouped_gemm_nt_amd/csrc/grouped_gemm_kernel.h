@@ -271,18 +271,64 @@ __device__ __forceinline__ long first_tile() {
 // of the grid size, and L is left at the tile returned.
 constexpr int kKGroupM = 8;  // K-grouped tile order: m-tiles per group (see decode_tile)
 
-template <class T, int VAR, int DT, int GRAN>
-__device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Params& p, long& L) {
+// The tile context is the same for every lane of a wave, but the scheduler tables it is
+// decoded from are read from LDS into vector registers. Each value read from a table goes
+// through wave_uniform (one readfirstlane), so that everything derived from it is computed
+// in scalar registers and the decoded context does not hold ~25 vector registers through
+// the slice loop.
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint32_t wave_uniform(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+__device__ __forceinline__ long wave_uniform(long v) {
+  const uint64_t u = (uint64_t)v;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return (long)(((uint64_t)hi << 32) | lo);
+}
+template <class P>
+__device__ __forceinline__ P* wave_uniform(P* v) {
+  return reinterpret_cast<P*>(wave_uniform(reinterpret_cast<long>(v)));
+}
+// Every field of a decoded context (most are already scalar; this pins the rest).
+__device__ __forceinline__ void make_uniform(TileCtx& t) {
+  t.valid = wave_uniform(t.valid);
+  t.g = wave_uniform(t.g);
+  t.m0 = wave_uniform(t.m0);
+  t.n0 = wave_uniform(t.n0);
+  t.n_end = wave_uniform(t.n_end);
+  t.nk = wave_uniform(t.nk);
+  t.k_bytes = wave_uniform(t.k_bytes);
+  t.a_lim = wave_uniform(t.a_lim);
+  t.row_end = wave_uniform(t.row_end);
+  t.a_base = wave_uniform(t.a_base);
+  t.a_bytes = wave_uniform(t.a_bytes);
+  t.b_base = wave_uniform(t.b_base);
+  t.b_bytes = wave_uniform(t.b_bytes);
+  t.b_row0 = wave_uniform(t.b_row0);
+  t.lda = wave_uniform(t.lda);
+  t.ldb = wave_uniform(t.ldb);
+  t.sfa_off = wave_uniform(t.sfa_off);
+  t.sfa_ld = wave_uniform(t.sfa_ld);
+  t.sfb_off = wave_uniform(t.sfb_off);
+  t.sfb_ld = wave_uniform(t.sfb_ld);
+  t.d_base = wave_uniform(t.d_base);
+  t.d_bytes = wave_uniform(t.d_bytes);
+}
+
+template <class T, int VAR, int DT, int GRAN, bool PIN>
+__device__ __forceinline__ TileCtx decode_fields(const Sched<T, VAR>& S, const Params& p, long& L) {
+  auto pin = [](int v) { return PIN ? wave_uniform(v) : v; };
   TileCtx t = {};  // valid == 0, null bases: an idle cursor copies nothing
   constexpr int esz = DT == kBF16 ? 2 : 1;  // activation bytes per element
   if constexpr (VAR == kMasked || VAR == kPsum) {
     if (L < S.total) {
       const Piece q = piece_of(L, S.split_base, S.split_p);
-      const int g = expert_of_tile(q.tile, S.s_a, p.G);
-      const int c = S.s_b[g];
+      const int g = pin(expert_of_tile(q.tile, S.s_a, p.G));
+      const int c = pin(S.s_b[g]);
       const int mt_g = (c + T::BM - 1) / T::BM;
       int mt, nt;
-      expert_tile((int)(q.tile - S.s_a[g]), mt_g, &mt, &nt);
+      expert_tile((int)(q.tile - pin(S.s_a[g])), mt_g, &mt, &nt);
       const int Kb = p.K * esz;
       const int KB = p.K / 128;
       t.valid = 1;
@@ -298,7 +344,7 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       // resources start at the tile's first row (and first weight row), so 32-bit offsets
       // never span more than one tile whatever the operand sizes, and end at its last
       // valid row: the padding rows of a masked block read as zeros without being fetched.
-      const long r0 = VAR == kPsum ? (long)S.s_c[g] : (long)g * p.rows;
+      const long r0 = VAR == kPsum ? (long)pin(S.s_c[g]) : (long)g * p.rows;
       const long rt = min((long)T::BM, (long)c - t.m0);  // valid rows of the tile
       const int Kbw = DT == kFP4W ? Kb / 2 : Kb;  // weight bytes per row
       t.a_base = p.A + (r0 + t.m0) * Kb;
@@ -326,7 +372,7 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       const Piece q = piece_of(L, S.split_base, S.split_p);
       int block, sub, nt;
       contiguous_tile(q.tile, S.ntn, SUB, &block, &sub, &nt);
-      const int packed = S.s_b[block];
+      const int packed = pin(S.s_b[block]);
       const int blk = (packed >> 12) & 0xfff, e = packed & 0xfff, nsub = packed >> 24;
       const int m0 = blk * kContigBlock + sub * T::BM;
       // A sub-tile that starts on padding is padding throughout (valid rows come first
@@ -411,6 +457,16 @@ __device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Par
       break;
     }
   }
+  return t;
+}
+
+// PIN: whether the context is moved to scalar registers. It relieves the vector registers
+// of every tile that runs close to its register limit; the contiguous layout with UE8M0
+// scales, which has room and decodes a new tile every few slices, runs faster without.
+template <class T, int VAR, int DT, int GRAN, bool PIN = true>
+__device__ __forceinline__ TileCtx decode_tile(const Sched<T, VAR>& S, const Params& p, long& L) {
+  TileCtx t = decode_fields<T, VAR, DT, GRAN, PIN>(S, p, L);
+  if constexpr (PIN) make_uniform(t);
   return t;
 }
 
@@ -1064,7 +1120,8 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
   // ---- the pipeline
   long Li = first_tile();
   Issue ic;  // issue cursor
-  ic.t = decode_tile<T, VAR, DT, GRAN>(Sd, p, Li);
+  constexpr bool kPin = !(VAR == kContig && SF == kSfUE8M0);
+  ic.t = decode_tile<T, VAR, DT, GRAN, kPin>(Sd, p, Li);
   long Lc = Li;
   TileCtx tc = ic.t;  // compute cursor
   if (!tc.valid) return;
@@ -1072,7 +1129,7 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
   auto advance = [&](TileCtx& t, long& L, int& s) -> bool {
     if (t.valid && ++s >= t.nk) {
       L += grid;
-      t = decode_tile<T, VAR, DT, GRAN>(Sd, p, L);
+      t = decode_tile<T, VAR, DT, GRAN, kPin>(Sd, p, L);
       s = 0;
       return true;
     }

@@ -389,12 +389,20 @@ WORKLOADS = {
                            expected_m=113, seed=2, sf_fmt="ue8m0", rows_per_expert_max=256),
     "contig_fp8_w2": dict(variant="contiguous", dtype="fp8", G=288, N=4096, K=256, lam=113,
                           expected_m=113, seed=3, sf_fmt="ue8m0", rows_per_expert_max=256),
+    # the w13 shape with float32 scales and per-channel weight scales
+    "contig_fp8ch_w13": dict(variant="contiguous", dtype="fp8", G=288, N=512, K=4096,
+                             lam=113, expected_m=113, seed=2, sfb_gran="channel",
+                             rows_per_expert_max=256),
     "masked_fp8_g32_n6144": dict(variant="masked", dtype="fp8", G=32, cap=4096, N=6144,
                                  K=7168, lam=192, expected_m=192, seed=4),
     "masked_bf16_g32_n6144": dict(variant="masked", dtype="bf16", G=32, cap=4096, N=6144,
                                   K=7168, lam=192, expected_m=192, seed=4),
     "masked_fp8_g6_n4096": dict(variant="masked", dtype="fp8", G=6, cap=4096, N=4096,
                                 K=4096, lam=1024, expected_m=1024, seed=5),
+    # the same shape with float32 per-channel weight scales (1 x 128 along K per weight row)
+    "masked_fp8ch_g6_n4096": dict(variant="masked", dtype="fp8", G=6, cap=4096, N=4096,
+                                  K=4096, lam=1024, expected_m=1024, seed=5,
+                                  sfb_gran="channel"),
     # FP8 activations x FP4 weights (1x32 UE8M0 weight scales) on the same shapes
     "contig_fp4_w13": dict(variant="contiguous", dtype="fp8_fp4", G=288, N=512, K=4096,
                            lam=113, expected_m=113, seed=2, sf_fmt="ue8m0",

@@ -397,6 +397,7 @@ def test_kgrouped_routing_beyond_int32(mode):
 @pytest.mark.parametrize("variant", ["masked", "contiguous", "psum"])
 @pytest.mark.parametrize("dtype,sf_fmt,gran", [
     ("fp8", "f32", "block128"),
+    ("fp8", "f32", "channel"),  # contiguous: the four-wave 128 x 256 tile
     ("fp8", "ue8m0", "channel"),
     ("bf16", "f32", "block128"),
 ])
