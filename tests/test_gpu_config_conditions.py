@@ -156,7 +156,8 @@ def test_cfg4_fused_chain_graph_replay_redrawn_routing_full_size():
 
 
 @pytest.mark.parametrize("name", ["masked_fp8_g32_n6144", "masked_bf16_g32_n6144",
-                                  "masked_fp8_g6_n4096", "masked_bf16_g6_n4096"])
+                                  "masked_fp8_g6_n4096", "masked_bf16_g6_n4096",
+                                  "masked_fp8ch_g6_n4096"])
 def test_cfg5_whole_experts(name):
     """Every row and column of the largest and the smallest non-empty expert, plus the
     sentinel on every byte outside the valid rows of all experts."""
@@ -184,7 +185,8 @@ def _runner(name):
 
 
 @pytest.mark.parametrize("name", ["masked_bf16_repro", "masked_fp8_g32_n1536", "contig_fp8_w13",
-                                  "masked_fp8_g6_n4096"])
+                                  "masked_fp8_g6_n4096", "masked_fp8ch_g6_n4096",
+                                  "contig_fp8ch_w13"])
 def test_1000_calls_bitwise(name):
     say("1000 calls", name)
     p, shape, run = _runner(name)

@@ -39,7 +39,7 @@ def test_cfg_masked_fp8_g32_n1536_full():
     assert_report(check_masked(p, D), "fp8")
 
 
-@pytest.mark.parametrize("name", ["contig_fp8_w13", "contig_fp8_w2"])
+@pytest.mark.parametrize("name", ["contig_fp8_w13", "contig_fp8_w2", "contig_fp8ch_w13"])
 def test_cfg_contiguous_g288(name):
     say("cfg", name)
     p, opt = synth.make_workload(name, DEV)
@@ -57,7 +57,8 @@ def test_cfg_contiguous_g288(name):
 
 
 @pytest.mark.parametrize("name", ["masked_fp8_g32_n6144", "masked_bf16_g32_n6144",
-                                  "masked_fp8_g6_n4096", "masked_bf16_g6_n4096"])
+                                  "masked_fp8_g6_n4096", "masked_bf16_g6_n4096",
+                                  "masked_fp8ch_g6_n4096"])
 def test_cfg_masked_large(name):
     say("cfg", name)
     p, opt = synth.make_workload(name, DEV)
