@@ -309,6 +309,13 @@ __device__ __forceinline__ void dma_x4(uint32_t lds, v4i rsrc, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(l), "v"(voff), "s"(rsrc) : "memory");
 }
+// The same copy with the streaming (non-temporal) cache policy, for operand bytes that
+// are read once.
+__device__ __forceinline__ void dma_x4_nt(uint32_t lds, v4i rsrc, uint32_t voff) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :: "s"(l), "v"(voff), "s"(rsrc) : "memory");
+}
 __device__ __forceinline__ void dma_x1(uint32_t lds, v4i rsrc, uint32_t voff) {
   const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
