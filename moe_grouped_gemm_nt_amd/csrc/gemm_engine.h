@@ -98,10 +98,13 @@ struct Params {
 // 128-byte K slices in LDS. SWI: the fused SwiGLU tile of the contiguous product, whose
 // 256 weight rows are the gate rows and then the up rows of 128 output columns, one
 // wave row-band covering all of them (so a row's 1x128 output group stays in one wave).
-template <int BM_, int BN_, int WM_, int WN_, int S_, bool SWI_ = false>
+// STREAMW: the weight copies take the streaming cache policy (every weight panel of the
+// call is read once).
+template <int BM_, int BN_, int WM_, int WN_, int S_, bool SWI_ = false, bool STREAMW_ = false>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_;
   static constexpr bool SWI = SWI_;
+  static constexpr bool STREAMW = STREAMW_;
   static_assert(!SWI || (BN == 256 && WN == 1), "fused SwiGLU tile: 256 weight rows, one wave column");
   static constexpr int NMW = WM * WN;  // MFMA waves
   static_assert(NMW == 4 || NMW == 8, "four or eight MFMA waves");

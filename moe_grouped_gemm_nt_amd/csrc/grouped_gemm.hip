@@ -51,6 +51,8 @@ using TileL8 = Tile<128, 256, 2, 4, 3>;
 using TileSwi = Tile<128, 256, 8, 1, 3, true>;
 using TileSwi2 = Tile<128, 256, 8, 1, 2, true>;
 using TileK = Tile<64, 128, 2, 2, 3>;    // K-grouped output tiles
+template <class T>  // the same tile with streaming weight copies
+using Streamed = Tile<T::BM, T::BN, T::WM, T::WN, T::S, T::SWI, true>;
 
 enum TileId { kTileS = 0, kTileM = 1, kTileL = 2, kTileL4 = 3 };
 
@@ -84,6 +86,15 @@ bool dev_info(DevInfo* out) {
 }
 
 long cdiv(long a, long b) { return (a + b - 1) / b; }
+
+// Bytes of the weight operand of an M-grouped call ([G][N][K] elements), and the size from
+// which a masked call whose experts fit one small m-tile streams its weights (below it the
+// weights stay cache-resident from call to call, and the hint only costs).
+long weight_bytes(mgg_dtype dt, int G, int N, int K) {
+  const long e = (long)G * N * K;
+  return dt == MGG_BF16 ? 2 * e : dt == MGG_FP8_FP4 ? e / 2 : e;
+}
+constexpr long kStreamWeightBytes = 64L << 20;
 
 // Bytes the scheduler keeps in LDS after the pipeline stages, and the transient scan
 // scratch it needs inside the stages.
@@ -160,7 +171,17 @@ long m_tiles(const Params& p) {
 }
 
 template <int VAR, int DT, int SF, int GRAN>
-mgg_status launch_tile(TileId tile, const Params& p, hipStream_t s) {
+mgg_status launch_tile(TileId tile, const Params& p, hipStream_t s, bool stream_w) {
+  // Masked calls whose experts fit in one 32- or 64-row m-tile and whose weights are large
+  // read every weight panel once: their copies of it take the streaming policy.
+  if constexpr (VAR == kMasked) {
+    if (stream_w && tile == kTileS) {
+      using TS = std::conditional_t<DT == kBF16, TileS16, TileS8>;
+      return launch<Streamed<TS>, VAR, DT, SF, GRAN, false>(p, m_tiles<TS, VAR>(p), s);
+    }
+    if (stream_w && tile == kTileM)
+      return launch<Streamed<TileM>, VAR, DT, SF, GRAN, false>(p, m_tiles<TileM, VAR>(p), s);
+  }
   if constexpr (VAR == kMasked && DT == kFP8) {
     if (tile == kTileL4 && lds_bytes<TileL, VAR, DT, SF, GRAN, false>(p) <= kLdsBytes)
       return launch<TileL, VAR, DT, SF, GRAN, false>(p, m_tiles<TileL, VAR>(p), s);
@@ -182,16 +203,16 @@ mgg_status launch_tile(TileId tile, const Params& p, hipStream_t s) {
 
 // Dispatch over the compile-time parameters of the M-grouped variants.
 template <int VAR>
-mgg_status dispatch_m(mgg_dtype dt, mgg_sf_fmt sf, mgg_sfb_gran gran, TileId tile,
+mgg_status dispatch_m(mgg_dtype dt, mgg_sf_fmt sf, mgg_sfb_gran gran, TileId tile, bool stream_w,
                       const Params& p, hipStream_t s) {
-  if (dt == MGG_BF16) return launch_tile<VAR, kBF16, kSfF32, kSfbBlock>(tile, p, s);
-  if (dt == MGG_FP8_FP4) return launch_tile<VAR, kFP4W, kSfUE8M0, kSfbBlock32>(tile, p, s);
+  if (dt == MGG_BF16) return launch_tile<VAR, kBF16, kSfF32, kSfbBlock>(tile, p, s, stream_w);
+  if (dt == MGG_FP8_FP4) return launch_tile<VAR, kFP4W, kSfUE8M0, kSfbBlock32>(tile, p, s, stream_w);
   if (sf == MGG_SF_F32) {
-    if (gran == MGG_SFB_BLOCK128) return launch_tile<VAR, kFP8, kSfF32, kSfbBlock>(tile, p, s);
-    return launch_tile<VAR, kFP8, kSfF32, kSfbChannel>(tile, p, s);
+    if (gran == MGG_SFB_BLOCK128) return launch_tile<VAR, kFP8, kSfF32, kSfbBlock>(tile, p, s, stream_w);
+    return launch_tile<VAR, kFP8, kSfF32, kSfbChannel>(tile, p, s, stream_w);
   }
-  if (gran == MGG_SFB_BLOCK128) return launch_tile<VAR, kFP8, kSfUE8M0, kSfbBlock>(tile, p, s);
-  return launch_tile<VAR, kFP8, kSfUE8M0, kSfbChannel>(tile, p, s);
+  if (gran == MGG_SFB_BLOCK128) return launch_tile<VAR, kFP8, kSfUE8M0, kSfbBlock>(tile, p, s, stream_w);
+  return launch_tile<VAR, kFP8, kSfUE8M0, kSfbChannel>(tile, p, s, stream_w);
 }
 
 // The fused SwiGLU tile with three stages, or with two when the contiguous layout's
@@ -357,7 +378,8 @@ mgg_status grouped_gemm_masked(mgg_dtype dt, int G, int cap, int N, int K, const
   p.meta_bytes = (uint32_t)G * 4;
   TileId tile = pick_tile(expected_m, cap);
   if (tile == kTileL && expected_m > 128 && expected_m <= 256) tile = kTileL4;
-  return dispatch_m<kMasked>(dt, sf, gran, tile, p, stream);
+  return dispatch_m<kMasked>(dt, sf, gran, tile, weight_bytes(dt, G, N, K) >= kStreamWeightBytes,
+                            p, stream);
 }
 
 mgg_status grouped_gemm_contiguous(mgg_dtype dt, int G, int M, int N, int K, const void* A,
@@ -393,7 +415,7 @@ mgg_status grouped_gemm_contiguous(mgg_dtype dt, int G, int M, int N, int K, con
   p.sfa_bytes = dt != MGG_BF16 ? scale_bytes(sfa_n, sf) : 0;
   p.sfb_bytes = dt != MGG_BF16 ? scale_bytes(sfb_n, sf) : 0;
   p.meta_bytes = (uint32_t)M * 4;
-  return dispatch_m<kContig>(dt, sf, gran, pick_tile(expected_m, kContigBlock), p, stream);
+  return dispatch_m<kContig>(dt, sf, gran, pick_tile(expected_m, kContigBlock), false, p, stream);
 }
 
 mgg_status grouped_gemm_contiguous_psum(mgg_dtype dt, int G, int M, int N, int K,
@@ -428,7 +450,7 @@ mgg_status grouped_gemm_contiguous_psum(mgg_dtype dt, int G, int M, int N, int K
   p.sfa_bytes = dt != MGG_BF16 ? scale_bytes(sfa_n, sf) : 0;
   p.sfb_bytes = dt != MGG_BF16 ? scale_bytes(sfb_n, sf) : 0;
   p.meta_bytes = (uint32_t)G * 4;
-  return dispatch_m<kPsum>(dt, sf, gran, pick_tile(expected_m, kContigBlock), p, stream);
+  return dispatch_m<kPsum>(dt, sf, gran, pick_tile(expected_m, kContigBlock), false, p, stream);
 }
 
 mgg_status grouped_gemm_contiguous_swiglu_quant(mgg_dtype dt, int G, int M, int I, int K,
