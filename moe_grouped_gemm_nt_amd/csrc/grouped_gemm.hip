@@ -53,6 +53,15 @@ using TileSwi2 = Tile<128, 256, 8, 1, 2, true>;
 using TileK = Tile<64, 128, 2, 2, 3>;    // K-grouped output tiles
 template <class T>  // the same tile with streaming weight copies
 using Streamed = Tile<T::BM, T::BN, T::WM, T::WN, T::S, T::SWI, true>;
+// The 32-row tile of a dtype, and the 128x256 tile of a variant: contiguous FP8 calls with
+// float32 per-channel weight scales take the four-wave tile (with eight waves they need
+// more than the 168 registers three waves per SIMD leave).
+template <int DT>
+using SmallTile = std::conditional_t<DT == kBF16, TileS16, TileS8>;
+template <int VAR, int DT, int SF, int GRAN>
+using LargeTile = std::conditional_t<DT == kBF16 || (VAR == kContig && DT == kFP8 &&
+                                                     SF == kSfF32 && GRAN == kSfbChannel),
+                                     TileL, TileL8>;
 
 enum TileId { kTileS = 0, kTileM = 1, kTileL = 2, kTileL4 = 3 };
 
@@ -172,11 +181,27 @@ long m_tiles(const Params& p) {
 
 template <int VAR, int DT, int SF, int GRAN>
 mgg_status launch_tile(TileId tile, const Params& p, hipStream_t s, bool stream_w) {
-  // Masked calls whose experts fit in one 32- or 64-row m-tile and whose weights are large
-  // read every weight panel once: their copies of it take the streaming policy.
+  // Calls that read every weight panel once stream their weight copies (stream_w, chosen
+  // by the entry point): masked calls whose experts fit in one 32- or 64-row m-tile and
+  // whose weights are large, and contiguous calls with at most 512 bytes of K (w2-like:
+  // each expert's one or two m-tiles read their panel over a few slices while the output
+  // writes are as large as the weight reads).
+  if constexpr (VAR == kContig) {
+    if (stream_w) {
+      if (tile == kTileL4) tile = kTileL;
+      using TLg = LargeTile<VAR, DT, SF, GRAN>;
+      using TS = SmallTile<DT>;
+      if (tile == kTileL && lds_bytes<TLg, VAR, DT, SF, GRAN, false>(p) > kLdsBytes) tile = kTileM;
+      switch (tile) {
+        case kTileS: return launch<Streamed<TS>, VAR, DT, SF, GRAN, false>(p, m_tiles<TS, VAR>(p), s);
+        case kTileM: return launch<Streamed<TileM>, VAR, DT, SF, GRAN, false>(p, m_tiles<TileM, VAR>(p), s);
+        default: return launch<Streamed<TLg>, VAR, DT, SF, GRAN, false>(p, m_tiles<TLg, VAR>(p), s);
+      }
+    }
+  }
   if constexpr (VAR == kMasked) {
     if (stream_w && tile == kTileS) {
-      using TS = std::conditional_t<DT == kBF16, TileS16, TileS8>;
+      using TS = SmallTile<DT>;
       return launch<Streamed<TS>, VAR, DT, SF, GRAN, false>(p, m_tiles<TS, VAR>(p), s);
     }
     if (stream_w && tile == kTileM)
@@ -188,12 +213,10 @@ mgg_status launch_tile(TileId tile, const Params& p, hipStream_t s, bool stream_
   }
   if (tile == kTileL4) tile = kTileL;
   // The largest tile needs the most LDS; fall back to the middle one when the
-  // scheduler table does not fit next to it. Contiguous FP8 calls with float32
-  // per-channel weight scales take the four-wave 128x256 tile: with eight waves they need
-  // more than the 168 registers three waves per SIMD leave.
-  using TileLg = std::conditional_t<DT == kBF16 || (VAR == kContig && DT == kFP8 && SF == kSfF32 && GRAN == kSfbChannel), TileL, TileL8>;
+  // scheduler table does not fit next to it.
+  using TileLg = LargeTile<VAR, DT, SF, GRAN>;
   if (tile == kTileL && lds_bytes<TileLg, VAR, DT, SF, GRAN, false>(p) > kLdsBytes) tile = kTileM;
-  using TileS = std::conditional_t<DT == kBF16, TileS16, TileS8>;
+  using TileS = SmallTile<DT>;
   switch (tile) {
     case kTileS: return launch<TileS, VAR, DT, SF, GRAN, false>(p, m_tiles<TileS, VAR>(p), s);
     case kTileM: return launch<TileM, VAR, DT, SF, GRAN, false>(p, m_tiles<TileM, VAR>(p), s);
@@ -415,7 +438,9 @@ mgg_status grouped_gemm_contiguous(mgg_dtype dt, int G, int M, int N, int K, con
   p.sfa_bytes = dt != MGG_BF16 ? scale_bytes(sfa_n, sf) : 0;
   p.sfb_bytes = dt != MGG_BF16 ? scale_bytes(sfb_n, sf) : 0;
   p.meta_bytes = (uint32_t)M * 4;
-  return dispatch_m<kContig>(dt, sf, gran, pick_tile(expected_m, kContigBlock), false, p, stream);
+  const bool short_k = (long)K * (dt == MGG_BF16 ? 2 : 1) <= 512;
+  return dispatch_m<kContig>(dt, sf, gran, pick_tile(expected_m, kContigBlock), short_k, p,
+                             stream);
 }
 
 mgg_status grouped_gemm_contiguous_psum(mgg_dtype dt, int G, int M, int N, int K,

@@ -665,11 +665,9 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
       // FP4 weight rows advance 64 bytes per slice (K is a multiple of 128: no tail)
       uint32_t voff = I.vab[u] + (Lay::FP4W && u >= Lay::U_A ? s * Lay::B_ROW : kb0);
       if (!Lay::FP4W && !full && kb0 + c16 + 16 > t.k_bytes) voff = kOOB;
-      // Weight rows read once stream past the caches: tiles built for it (STREAMW), and a
-      // contiguous call with at most 512 bytes of K (w2-like: each expert's one or two
-      // m-tiles read their panel over a few slices while the output writes are as large
-      // as the weight reads).
-      if (u >= Lay::U_A && (T::STREAMW || (VAR == kContig && !T::SWI && t.k_bytes <= 512)))
+      // Weight rows read once stream past the caches (tiles built for it, chosen on the
+      // host).
+      if (u >= Lay::U_A && T::STREAMW)
         dma_x4_nt(st + Lay::A_OFF + 1024 * (4 * u + cwave), I.rs_b, voff);
       else
         dma_x4(st + Lay::A_OFF + 1024 * (4 * u + cwave), u < Lay::U_A ? I.rs_a : I.rs_b, voff);
