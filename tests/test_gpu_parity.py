@@ -427,3 +427,27 @@ def test_split_last_round_ragged_n(variant, dtype, sf_fmt, gran):
         outs.append(bf16_bits(D))
     assert_report(check(p, D), dtype)
     assert (outs[0] == outs[1]).all(), "the split tile disagrees with the 32-row tile"
+
+
+# Masked calls whose expected rows pick the 32- or 64-row tile and whose weights reach
+# 64 MB run that tile's streamed twin (weight copies with the streaming cache policy). The
+# policy changes no value: every valid row against the oracle, every padding byte keeps
+# its sentinel, and the 32-row and 64-row tiles give the same bits.
+@pytest.mark.parametrize("dtype", ["fp8", "bf16"])
+def test_masked_streamed_small_tiles(dtype):
+    G, N, K = (8, 4096, 2048) if dtype == "fp8" else (4, 4096, 2048)  # 64 MiB of weights
+    esz = 1 if dtype == "fp8" else 2
+    assert G * N * K * esz >= 64 << 20
+    rng = np.random.default_rng(71)
+    counts = rng.integers(0, 65, size=G)
+    counts[[0, G - 1]] = [64, 1]
+    say("streamed small tiles", dtype, counts.tolist())
+    p = synth.make_masked(dtype, G, 64, N, K, counts, seed=71, device=DEV)
+    outs = []
+    for em in (16, 48):  # the 32-row tile, then the 64-row tile (both streamed)
+        say("  expected_m", em)
+        D = run_masked(p, em)
+        torch.cuda.synchronize()
+        outs.append(bf16_bits(D))
+    assert_report(check_masked(p, D), dtype)
+    assert (outs[0] == outs[1]).all(), "the 32- and 64-row streamed tiles disagree"
