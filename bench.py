@@ -119,6 +119,14 @@ def parse():
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="(no GPU) write profiles/<workload>_kernel_trace.md from the csv "
                          "output of `rocprofv3 --kernel-trace --stats` of this script")
+    ap.add_argument("--summarize-counters", metavar="PREFIX",
+                    help="(no GPU) write profiles/<workload>_counters.md from the csv output of "
+                         "the four `rocprofv3 --pmc` passes in PREFIX_1 .. PREFIX_4 (counter "
+                         "lists in COUNTER_PASSES)")
+    ap.add_argument("--summarize-mfma-busy", metavar="PREFIX",
+                    help="(no GPU) write profiles/grouped_gemm_kernel_mfma_busy_and_clock.md from "
+                         "the csv output of one `rocprofv3 --pmc` run per workload in "
+                         "PREFIX<workload> (counters in MFMA_BUSY_COUNTERS)")
     ap.add_argument("--summarize-traffic", nargs=4,
                     metavar=("COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
                     help="(no GPU) write profiles/<workload>_hbm_traffic.md from the csv "
@@ -182,6 +190,9 @@ def algorithmic_bytes(p, opt) -> int:
 
 def main():
     args = parse()
+    if args.summarize_counters or args.summarize_mfma_busy:
+        summarize_counters(args)
+        return
     if args.summarize_trace or args.summarize_traffic:
         summarize(args)
         return
@@ -592,6 +603,173 @@ def _counter_median(directory, kernel_sub):
     if not vals:
         raise SystemExit(f"no {kernel_sub} dispatches in {directory}")
     return statistics.median(vals), len(vals)
+
+
+# Counter passes behind profiles/<workload>_counters.md (each within one run's limits of
+# the hardware's counter blocks), and the one-run counter set of the MFMA-busy table.
+COUNTER_PASSES = [
+    "SQ_WAVES SQ_BUSY_CYCLES SQ_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES "
+    "SQ_INSTS_MFMA SQ_ACTIVE_INST_VALU SQ_INSTS_VALU_FMA_F32 GRBM_GUI_ACTIVE GRBM_COUNT",
+    "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_LDS "
+    "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_DATA_FIFO_FULL",
+    "TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_LEVEL_sum",
+    "TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_READ_REQ_sum TCP_PENDING_STALL_CYCLES_sum "
+    "TCP_TCR_TCP_STALL_CYCLES_sum TA_BUFFER_READ_LDS_WAVEFRONTS_sum TA_TA_BUSY_sum",
+]
+MFMA_BUSY_COUNTERS = "SQ_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_WAVES GRBM_GUI_ACTIVE"
+MFMA_BUSY_WORKLOADS = ["masked_fp8_g6_n4096", "masked_bf16_g6_n4096", "masked_fp8_g32_n6144",
+                       "masked_bf16_g32_n6144", "contig_fp8_w13", "contig_fp8_w2"]
+N_CUS, N_XCDS, N_SIMDS, N_L2_CHANNELS = 256, 8, 1024, 128
+
+
+def _dispatch_medians(directory):
+    """{counter: median over the dispatches of the GEMM kernel} (each dispatch summed over
+    the rows rocprofv3 writes for it), and the kernel name."""
+    import statistics
+    by, name = {}, None
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if KERNEL_NAME not in r["Kernel_Name"]:
+            continue
+        name = r["Kernel_Name"]
+        d = by.setdefault(r["Counter_Name"], {})
+        d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not by:
+        raise SystemExit(f"no {KERNEL_NAME} dispatches in {directory}")
+    return {k: statistics.median(v.values()) for k, v in by.items()}, name
+
+
+def _trace_average_us(workload):
+    """Average launch time of the GEMM kernel in profiles/<workload>_kernel_trace.md."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_kernel_trace.md")
+    m = re.search(r"grouped_gemm_kernel<[^|]*\| (\d+) \| (\d+) \|", open(path).read())
+    if not m:
+        raise SystemExit(f"no kernel average in {path}")
+    return int(m.group(2)) / 1000.0
+
+
+def summarize_counters(args):
+    """The counter summaries under profiles/ (medians over the dispatches; readings derived
+    from the chip's 256 CUs, 8 XCDs, 1024 SIMDs and 128 L2 channels)."""
+    from moe_grouped_gemm_nt_amd import synth
+    out_dir = os.path.join(ROOT, "profiles")
+    dig = kernel_source_digest(KERNEL_NAME)
+    cd = "`cd /tmp && export TMPDIR=/tmp` first, then back to the root"
+    run = ("timeout -s KILL 150 rocprofv3 --kernel-include-regex grouped_gemm_kernel --pmc {c} "
+           "-d {d} -o w --output-format csv -- python -u bench.py --workload {w} --steps 20 "
+           "--warmup 2 --no-cpu-baseline")
+    if args.summarize_counters:
+        w, pre = args.workload, args.summarize_counters
+        c, kname = {}, None
+        for i in range(1, len(COUNTER_PASSES) + 1):
+            v, kname = _dispatch_medians(f"{pre}_{i}")
+            c.update(v)
+        tm = re.search(r"Tile<(\d+), (\d+), (\d+), (\d+), (\d+)", kname)
+        bm, bn, wm, wn = (int(tm.group(k)) for k in (1, 2, 3, 4))
+        cfg = synth.WORKLOADS[w]
+        slices = cfg["K"] * (2 if cfg["dtype"] == "bf16" else 1) // 128
+        mfma_per_slice = (bm // 16) * (bn // 16) if cfg["dtype"] != "bf16" else (bm // 32) * (bn // 32) * 4
+        nmw = wm * wn
+        if cfg["variant"] != "masked":
+            raise SystemExit("counter summaries are written for masked workloads")
+        counts = synth.poisson_counts(cfg["G"], cfg["lam"], cfg["cap"], cfg["seed"])
+        tiles = int(sum((int(n) + bm - 1) // bm for n in counts)) * ((cfg["N"] + bn - 1) // bn)
+        mfma_per_wave = mfma_per_slice // nmw  # per MFMA wave per slice
+        wave_slices = c["SQ_INSTS_MFMA"] / mfma_per_wave  # wave-slices that issued MFMAs
+        dur = _trace_average_us(w)
+        cyc = c["GRBM_GUI_ACTIVE"] / N_XCDS
+        ghz = cyc / (dur * 1e3)
+        rows = []
+
+        def r(name, val, reading):
+            rows.append(f"| {name} | {val} | {reading} |")
+        wpg = int(round(c["SQ_WAVES"] / N_CUS))
+        r("SQ_WAVES", f"{c['SQ_WAVES']:.0f}", f"{N_CUS} workgroups x {wpg} waves ({nmw} MFMA, {wpg - nmw} copy)")
+        r("GRBM_GUI_ACTIVE", f"{c['GRBM_GUI_ACTIVE']:.4g}", f"/ {N_XCDS} XCDs = {cyc / 1e3:.0f}k cycles over the {dur:.1f} us launch (trace average): shader clock ~{ghz:.2f} GHz (an estimate: counted launches can run a few percent longer)")
+        r("SQ_BUSY_CYCLES / SQ_CYCLES", f"{c['SQ_BUSY_CYCLES']:.4g} / {c['SQ_CYCLES']:.4g}", f"{100 * c['SQ_BUSY_CYCLES'] / c['SQ_CYCLES']:.1f} % of the launch has work on the shader engines")
+        full = tiles * slices * mfma_per_slice
+        r("SQ_INSTS_MFMA", f"{c['SQ_INSTS_MFMA']:.4g}", f"{100 * c['SQ_INSTS_MFMA'] / full:.1f} % of {tiles} tiles x {slices} slices x {mfma_per_slice} MFMAs ({full}): waves whose rows are all padding issue none; the whole chip is counted")
+        mb = c["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMDS
+        r("SQ_VALU_MFMA_BUSY_CYCLES", f"{c['SQ_VALU_MFMA_BUSY_CYCLES']:.4g}", f"= SQ_INSTS_MFMA x 32; / {N_SIMDS} SIMDs = {mb / 1e3:.0f}k cycles: the MFMA pipe is busy {100 * mb / cyc:.0f} % of the launch")
+        ce = c["SQ_VALU_MFMA_COEXEC_CYCLES"] / N_SIMDS
+        r("SQ_VALU_MFMA_COEXEC_CYCLES", f"{c['SQ_VALU_MFMA_COEXEC_CYCLES']:.4g}", f"/ {N_SIMDS} = {ce / 1e3:.0f}k cycles: VALU work runs beside the MFMA pipe for {100 * ce / mb:.0f} % of its busy cycles")
+        r("SQ_INSTS_VALU_FMA_F32", f"{c['SQ_INSTS_VALU_FMA_F32']:.4g}", f"the float32 promotion, one FMA per output element per slice: 4 per 16x16 MFMA ({4 * c['SQ_INSTS_MFMA']:.4g})")
+        r("SQ_ACTIVE_INST_VALU", f"{c['SQ_ACTIVE_INST_VALU']:.4g}", "")
+        per = c["SQ_INSTS_LDS"] / wave_slices
+        r("SQ_INSTS_LDS", f"{c['SQ_INSTS_LDS']:.4g}", f"fragment and scale reads: {per:.1f} per MFMA wave per slice that issues MFMAs, the epilogue included ({bm // wm} x {bn // wn} outputs per wave)")
+        r("SQ_LDS_BANK_CONFLICT / SQ_LDS_DATA_FIFO_FULL", f"{c['SQ_LDS_BANK_CONFLICT']:.0f} / {c['SQ_LDS_DATA_FIFO_FULL']:.0f}", "LDS bank conflicts and LDS data-path backups")
+        r("SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES", f"{c['SQ_WAIT_INST_LDS']:.4g} / {c['SQ_WAVE_CYCLES']:.4g}", f"{100 * c['SQ_WAIT_INST_LDS'] / c['SQ_WAVE_CYCLES']:.1f} % of wave-cycles wait on LDS data")
+        r("SQ_WAIT_ANY / SQ_WAVE_CYCLES", f"{c['SQ_WAIT_ANY']:.4g} / {c['SQ_WAVE_CYCLES']:.4g}", f"{100 * c['SQ_WAIT_ANY'] / c['SQ_WAVE_CYCLES']:.0f} % of wave-cycles wait on something (barriers, memory counters)")
+        hr = c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"])
+        r("TCC_HIT_sum / TCC_MISS_sum", f"{c['TCC_HIT_sum']:.4g} / {c['TCC_MISS_sum']:.4g}", f"L2 hit rate {100 * hr:.1f} %")
+        ea = c["TCC_EA0_RDREQ_sum"]
+        r("TCC_EA0_RDREQ_sum", f"{ea:.4g}", f"x 128 B = {ea * 128 / 1e6:.0f} MB read past L2 (Infinity Cache or HBM)")
+        lvl = c["TCC_EA0_RDREQ_LEVEL_sum"]
+        r("TCC_EA0_RDREQ_LEVEL_sum", f"{lvl:.4g}", f"/ requests: {lvl / ea:.0f} cycles per read past L2; / cycles: {lvl / cyc / 1e3:.1f}k reads in flight on average, {lvl / cyc / N_L2_CHANNELS:.0f} per L2 channel")
+        tr = c["TCP_TCC_READ_REQ_sum"]
+        r("TCP_TCC_READ_REQ_sum", f"{tr:.4g}", f"x 128 B = {tr * 128 / 1e9:.2f} GB from L2 into the CUs (the operand slices copied into LDS)")
+        lat = c["TCP_TCC_READ_REQ_LATENCY_sum"]
+        r("TCP_TCC_READ_REQ_LATENCY_sum", f"{lat:.4g}", f"{lat / tr:.0f} cycles per L1->L2 read on average; {lat / cyc / N_CUS:.0f} reads in flight per CU on average")
+        ps = c["TCP_PENDING_STALL_CYCLES_sum"] / N_CUS / cyc
+        r("TCP_PENDING_STALL_CYCLES_sum", f"{c['TCP_PENDING_STALL_CYCLES_sum']:.4g}", f"/ {N_CUS} CUs: the L1 cannot take a new request for lack of a pending-request slot {100 * ps:.0f} % of the cycles")
+        r("TCP_TCR_TCP_STALL_CYCLES_sum", f"{c['TCP_TCR_TCP_STALL_CYCLES_sum']:.4g}", f"/ {N_CUS}: the return path from L2 stalls {100 * c['TCP_TCR_TCP_STALL_CYCLES_sum'] / N_CUS / cyc:.1f} % of the cycles")
+        r("TA_TA_BUSY_sum", f"{c['TA_TA_BUSY_sum']:.4g}", f"/ {N_CUS}: texture address unit busy {100 * c['TA_TA_BUSY_sum'] / N_CUS / cyc:.0f} %")
+        r("TA_BUFFER_READ_LDS_WAVEFRONTS_sum", f"{c['TA_BUFFER_READ_LDS_WAVEFRONTS_sum']:.4g}", f"direct global->LDS copy instructions: {c['TA_BUFFER_READ_LDS_WAVEFRONTS_sum'] / (tiles * slices):.0f} per tile slice")
+        rows_txt = (f"per-expert rows {[int(n) for n in counts]}" if cfg["G"] <= 8
+                    else f"{int(counts.sum())} valid rows in all")
+        desc = (f"{cfg['G']} experts, capacity {cfg['cap']}, N = {cfg['N']}, K = {cfg['K']}, "
+                f"{rows_txt}, {cfg['dtype']} "
+                f"({cfg.get('sf_fmt', 'f32')} scales, {cfg.get('sfb_gran', 'block128')} weight scales): "
+                f"{tiles} tiles of {bm} x {bn} computed by {nmw} MFMA waves of {bm // wm} x {bn // wn}, "
+                f"{slices} slices each ({tiles / N_CUS:.2f} rounds of {N_CUS} workgroups)")
+        lines = [f"# grouped_gemm_kernel: SQ / L2 / L1 counters, workload {w}", "",
+                 f"The workload: {desc}.", "",
+                 f"Commands (repository root, one MI355X, {cd}), one pass per run:", ""]
+        for i, cs in enumerate(COUNTER_PASSES, 1):
+            lines.append("    " + run.format(c=cs, d=f"{pre}_{i}", w=w))
+        lines += ["", f"Summarised with `python bench.py --workload {w} --summarize-counters {pre}`: "
+                  "medians over the dispatches of `grouped_gemm_kernel` in each run (20 steps x 7 "
+                  "samples + 2 warmup); counters summed over the XCDs, shader engines and L2 "
+                  "channels of the dispatch:", "",
+                  "| Counter | Median | Reading |", "|---|---|---|"] + rows + \
+                 ["", f"kernel-source-sha256 of the profiled build: {dig}", ""]
+        path = os.path.join(out_dir, f"{w}_counters.md")
+        with open(path, "w") as f:
+            f.write("\n".join(lines))
+        print(f"wrote {path}")
+    if args.summarize_mfma_busy:
+        pre = args.summarize_mfma_busy
+        rows = []
+        for w in MFMA_BUSY_WORKLOADS:
+            c, _ = _dispatch_medians(f"{pre}{w}")
+            d = _trace_average_us(w)
+            cyc = c["GRBM_GUI_ACTIVE"] / N_XCDS
+            rows.append(f"| {w} | {d:.1f} | {c['SQ_CYCLES']:.4g} | {c['SQ_INSTS_MFMA']:.4g} | "
+                        f"{c['SQ_VALU_MFMA_BUSY_CYCLES']:.4g} | {cyc / (d * 1e3):.2f} | "
+                        f"{100 * c['SQ_VALU_MFMA_BUSY_CYCLES'] / N_SIMDS / cyc:.1f} % | "
+                        f"{100 * c['SQ_BUSY_CYCLES'] / c['SQ_CYCLES']:.0f} % |")
+        lines = ["# grouped_gemm_kernel: MFMA issue and shader clock, six GEMM workloads", "",
+                 f"Commands (repository root, one MI355X, {cd}), one run per workload `W` in "
+                 f"{', '.join(MFMA_BUSY_WORKLOADS)}:", "",
+                 "    " + run.format(c=MFMA_BUSY_COUNTERS, d=f"{pre}W", w="W"), "",
+                 f"Summarised with `python bench.py --summarize-mfma-busy {pre}`: medians over the "
+                 "dispatches of each run. `SQ_VALU_MFMA_BUSY_CYCLES` equals `SQ_INSTS_MFMA` x 32 in "
+                 "every run (the nominal issue time of a 16x16x128 FP8 or 32x32x16 BF16 MFMA), so "
+                 "\"MFMA busy\" below is the nominal MFMA time over the elapsed cycles of the "
+                 "dispatch; the elapsed cycles are `GRBM_GUI_ACTIVE` / 8 XCDs and the clock is "
+                 "those cycles over the kernel-trace average duration "
+                 "(`profiles/<W>_kernel_trace.md`).", "",
+                 "| Workload | Duration (us) | SQ_CYCLES | SQ_INSTS_MFMA | SQ_VALU_MFMA_BUSY_CYCLES | "
+                 "Clock (GHz) | MFMA busy at that clock | SQ busy |",
+                 "|---|---|---|---|---|---|---|---|"] + rows + ["",
+                 "The clock column is an estimate: the counted launches run under the profiler and "
+                 "can last a few percent longer than the traced ones, which is why the HBM-bound "
+                 "shapes can come out slightly above the 2.4 GHz maximum. The MFMA counts include "
+                 "the padding rows that the tiles compute.", "",
+                 f"kernel-source-sha256 of the profiled build: {dig}", ""]
+        path = os.path.join(out_dir, "grouped_gemm_kernel_mfma_busy_and_clock.md")
+        with open(path, "w") as f:
+            f.write("\n".join(lines))
+        print(f"wrote {path}")
 
 
 def summarize(args):

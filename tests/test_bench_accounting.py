@@ -139,3 +139,50 @@ def test_host_cpu_model_is_named():
     """The oracle baseline names the host CPU it ran on."""
     name = bench.host_cpu_model()
     assert isinstance(name, str) and name
+
+
+def _counter_csv(directory, dispatches):
+    """A rocprofv3-style counter_collection.csv: dispatches = {id: {counter: [values]}};
+    a counter with several values is written as several rows (summed per dispatch)."""
+    import csv
+    directory.mkdir(parents=True)
+    kname = "void mgg::grouped_gemm_kernel<mgg::Tile<128, 256, 2, 4, 3, false, false>, 0, 1, 0, 0, false>(mgg::Params)"
+    with open(directory / "w_counter_collection.csv", "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for d, cs in dispatches.items():
+            for name, vals in cs.items():
+                for v in vals:
+                    wr.writerow([d, kname, name, v])
+
+
+def test_counter_summary_arithmetic(tmp_path, monkeypatch):
+    """The counter summary sums a dispatch's rows, takes medians over dispatches, and
+    derives the clock, L2 hit rate and tile count from them and from the workload."""
+    import argparse
+    w = "masked_fp8_g6_n4096"
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / f"{w}_kernel_trace.md").write_text(
+        "| `void mgg::grouped_gemm_kernel<mgg::Tile<128, 256, 2, 4, 3, false, false>, 0, 1, 0, 0, "
+        "false>(mgg::Params)` | 7050 | 100000 | 90000 | 110000 | 1000 |\n")
+    names = [n for p in bench.COUNTER_PASSES for n in p.split()]
+    base = {n: 10.0 for n in names}
+    base.update({"GRBM_GUI_ACTIVE": 8 * 220000.0, "TCC_HIT_sum": 3.0, "TCC_MISS_sum": 1.0,
+                 "SQ_WAVES": 3072.0, "SQ_INSTS_MFMA": 816 * 32 * 128.0})
+    for i, p in enumerate(bench.COUNTER_PASSES, 1):
+        disp = {}
+        for d, scale in ((1, 0.5), (2, 1.0), (3, 3.0)):  # median dispatch: scale 1
+            disp[d] = {n: ([base[n] * scale / 2] * 2 if n == "TCC_HIT_sum" else [base[n] * scale])
+                       for n in p.split()}
+        _counter_csv(tmp_path / f"cnt_{i}", disp)
+    args = argparse.Namespace(workload=w, summarize_counters=str(tmp_path / "cnt"),
+                              summarize_mfma_busy=None)
+    bench.summarize_counters(args)
+    text = (tmp_path / "profiles" / f"{w}_counters.md").read_text()
+    assert "shader clock ~2.20 GHz" in text          # 220k cycles over 100 us
+    assert "L2 hit rate 75.0 %" in text              # 3 / (3 + 1), the hit rows summed
+    assert "816 tiles of 128 x 256" in text          # the workload's counts
+    assert "100.0 % of 816 tiles x 32 slices x 128 MFMAs" in text
+    assert "8 MFMA, 4 copy" in text
+    assert bench.kernel_source_digest(bench.KERNEL_NAME) in text
