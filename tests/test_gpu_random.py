@@ -29,7 +29,9 @@ def m_cases(n=72, seed=2026):
         dt, sf, gran = TYPES[rng.integers(len(TYPES))]
         G = int(rng.integers(1, 10))
         N = 8 * int(rng.integers(1, 49))
-        K = 128 * int(rng.integers(1, 5)) if dt != "bf16" else 8 * int(rng.integers(1, 65))
+        # K up to 1024 bytes per row: contiguous calls with at most 512 take the tiles
+        # with streamed weight copies, longer ones the plain tiles
+        K = 128 * int(rng.integers(1, 9)) if dt != "bf16" else 8 * int(rng.integers(1, 65))
         em = int(rng.choice([0, 8, 48, 200]))
         out.append(dict(case=c, variant=variant, dt=dt, sf=sf, gran=gran, G=G, N=N, K=K,
                         em=em, seed=int(rng.integers(1 << 30))))
