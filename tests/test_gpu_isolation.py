@@ -1,11 +1,12 @@
 """Bytes that no valid output depends on cannot change a valid output.
 
 A masked expert's rows at or past its count, their activation scales, the weights and
-weight scales of experts with no rows, and a contiguous or prefix-sum call's unrouted rows
-are filled with NaN bit patterns (bf16 0x7FC0, E4M3 0x7F, float32 NaN, UE8M0 0xFF; packed
-FP4 weights, which have no NaN, get the byte 0x7F) after a clean call. The call is then
-repeated on a fresh sentinel-filled output: every byte of it must equal the clean call's
-bytes, so valid rows are bit-identical and nothing is written outside them. The rows of
+weight scales of experts with no rows, a contiguous or prefix-sum call's unrouted rows and
+a K-grouped call's unrouted tokens are filled with NaN bit patterns (bf16 0x7FC0, E4M3
+0x7F, float32 NaN, UE8M0 0xFF; packed FP4 weights, which have no NaN, get the byte 0x7F)
+after a clean call. The call is then repeated on a fresh output: every byte of it must
+equal the clean call's bytes, so valid rows are bit-identical and nothing is written
+outside them. The rows of
 one expert are independent of each other in D = A B^T, so a NaN reaching a valid row can
 only come from a read across rows, experts or tiles; a control poisons one valid row and
 requires exactly that output row to change.
@@ -16,7 +17,7 @@ import pytest
 import torch
 
 from moe_grouped_gemm_nt_amd import synth
-from parity_util import bf16_bits, run_contiguous, run_masked, run_psum, say
+from parity_util import bf16_bits, run_contiguous, run_kgrouped, run_masked, run_psum, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -117,3 +118,34 @@ def test_unrouted_rows_poison(variant, dtype, sf_fmt, gran):
         torch.cuda.synchronize()
         diff = int((clean != dirty).sum())
         assert diff == 0, f"expected_m={em}: {diff} output bytes changed by poisoned inputs"
+
+
+@pytest.mark.parametrize("dtype,sf_fmt", [("bf16", "f32"), ("fp8", "f32"), ("fp8", "ue8m0")])
+@pytest.mark.parametrize("accumulate", [True, False])
+def test_kgrouped_unrouted_tokens_poison(dtype, sf_fmt, accumulate):
+    """The K-grouped call's token axis past the last expert (unrouted tokens of the packed
+    operands and their scale groups) does not reach any output."""
+    ks, M, N, K_total = [128, 0, 256, 384], 192, 264, 1024
+    T = sum(ks)
+    say("kgrouped poison", dtype, sf_fmt, accumulate)
+
+    def make():
+        return synth.make_kgrouped(dtype, ks, M, N, seed=47, device=DEV, std_a=1.0,
+                                   K_total=K_total, sf_fmt=sf_fmt)
+
+    def run(q):
+        D = torch.full((q.G, M, N), 0.25, dtype=torch.float32, device=DEV)
+        run_kgrouped(q, D, accumulate)
+        torch.cuda.synchronize()
+        return D.view(torch.int32).cpu().numpy()
+
+    clean = run(make())
+    q = make()
+    poison_rows(q.A[T * M:])
+    poison_rows(q.B[T * N:])
+    if q.SFA is not None:
+        poison_scales(q.SFA[T // 128:])
+        poison_scales(q.SFB[T // 128:])
+    dirty = run(q)
+    diff = int((clean != dirty).sum())
+    assert diff == 0, f"{diff} output words changed by poisoned unrouted tokens"
