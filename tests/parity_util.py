@@ -193,6 +193,15 @@ def run_contiguous(p: synth.Problem, expected_m=0, D=None):
     return D
 
 
+def cut_contiguous_rows(p: synth.Problem, M: int) -> synth.Problem:
+    """The first M rows of a contiguous problem (M need not be a multiple of 128)."""
+    idx = p.meta["m_indices"][:M]
+    return synth.Problem("contiguous", p.dtype, p.G, p.N, p.K, p.A[:M].contiguous(), p.B,
+                         None if p.SFA is None else p.SFA[:, :M].contiguous(), p.SFB,
+                         p.sf_fmt, p.sfb_gran, M=M, m_indices=p.m_indices[:M].contiguous(),
+                         meta={"m_indices": idx, "valid_rows": int((idx >= 0).sum())})
+
+
 def check_contiguous(p: synth.Problem, D: torch.Tensor, rows=None, cols=None,
                      check_sentinel=True):
     Dh = bf16_bits(D)

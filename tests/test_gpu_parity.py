@@ -13,8 +13,8 @@ import torch
 import oracle
 from moe_grouped_gemm_nt_amd import synth
 from parity_util import (SENTINEL, assert_report, bf16_bits, check_contiguous, check_kgrouped,
-                         check_masked, check_psum, run_contiguous, run_kgrouped, run_masked,
-                         run_psum, say)
+                         check_masked, check_psum, cut_contiguous_rows, run_contiguous,
+                         run_kgrouped, run_masked, run_psum, say)
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -175,6 +175,32 @@ def test_contiguous_ragged(dtype, sf_fmt, gran):
         outs.append(bf16_bits(D))
     assert_report(check_contiguous(p, D), dtype)
     assert (outs[0] == outs[1]).all() and (outs[1] == outs[2]).all(), "tile shapes disagree"
+
+
+@pytest.mark.parametrize("dtype,sf_fmt,gran", [
+    ("bf16", "f32", "block128"),
+    ("fp8", "f32", "block128"),
+    ("fp8", "ue8m0", "channel"),
+    ("fp8_fp4", "ue8m0", "block32"),
+])
+@pytest.mark.parametrize("M", [70, 326])
+def test_contiguous_total_rows_not_a_block_multiple(dtype, sf_fmt, gran, M):
+    """M = 70 (one partial block) and M = 326 (the last expert's block cut after its 70
+    valid rows): the rows past M are not part of the operands; every tile shape gives the
+    same bits and matches the oracle."""
+    segs = [70] if M == 70 else [130, 70]
+    say("contiguous rows", M, dtype, sf_fmt, gran)
+    full = synth.make_contiguous(dtype, len(segs), 264, 384, segs, seed=8, device=DEV,
+                                 sf_fmt=sf_fmt, sfb_gran=gran)
+    p = cut_contiguous_rows(full, M)
+    assert int(p.meta["m_indices"][-1]) == len(segs) - 1
+    outs = []
+    for em in (8, 64, 128):
+        D = run_contiguous(p, em)
+        torch.cuda.synchronize()
+        outs.append(bf16_bits(D))
+    assert_report(check_contiguous(p, D), dtype)
+    assert all((o == outs[0]).all() for o in outs), "tile shapes disagree"
 
 
 def test_contiguous_matches_masked_bitwise():

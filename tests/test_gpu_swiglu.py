@@ -17,7 +17,8 @@ import torch
 import oracle
 from moe_grouped_gemm_nt_amd import synth
 from parity_util import (assert_report, assert_swiglu_plain, bf16_bits, check_contiguous,
-                         compare_swiglu_to_plain, np_codes, say, sentinel_like)
+                         compare_swiglu_to_plain, cut_contiguous_rows, np_codes, say,
+                         sentinel_like)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -292,6 +293,20 @@ def test_fused_swiglu_matches_separate_steps(dt, sf, gran, sfq):
     Qf, SFf, Qs, SFs, valid, H = fused_vs_separate(p, sfq, z=1e-4)
     assert_fused_equal(Qf, SFf, Qs, SFs, valid)
     assert_fused_plain(H, Qf, SFf, valid, sfq, z=1e-4)
+
+
+@pytest.mark.parametrize("M", [70, 326])
+def test_fused_swiglu_total_rows_not_a_block_multiple(M):
+    """M = 70 and M = 326 (the last block cut after its expert's 70 rows): bit-identical
+    to GEMM -> SwiGLU + quantization on the same rows."""
+    segs = [70] if M == 70 else [130, 70]
+    say("fused rows", M)
+    full = synth.make_contiguous("fp8", len(segs), 768, 512, segs, seed=53, device=DEV,
+                                 sf_fmt="f32", sfb_gran="block128", std_b=0.05)
+    p = cut_contiguous_rows(full, M)
+    Qf, SFf, Qs, SFs, valid, H = fused_vs_separate(p, "ue8m0", z=1e-4)
+    assert_fused_equal(Qf, SFf, Qs, SFs, valid)
+    assert_fused_plain(H, Qf, SFf, valid, "ue8m0", z=1e-4)
 
 
 def test_fused_swiglu_full_w13_shape():
