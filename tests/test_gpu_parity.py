@@ -203,6 +203,45 @@ def test_contiguous_total_rows_not_a_block_multiple(dtype, sf_fmt, gran, M):
     assert all((o == outs[0]).all() for o in outs), "tile shapes disagree"
 
 
+@pytest.mark.parametrize("dtype,sf_fmt,gran", [
+    ("bf16", "f32", "block128"),
+    ("fp8", "f32", "block128"),
+    ("fp8", "ue8m0", "channel"),
+    ("fp8_fp4", "ue8m0", "block32"),
+])
+def test_smallest_shapes(dtype, sf_fmt, gran):
+    """The smallest sizes each entry point accepts: one expert, N = 8, K = 8 (BF16) or 128
+    (FP8), one row (masked capacity 1, contiguous and prefix-sum M = 1), and a K-grouped
+    call with M = 1, N = 8 and one group of tokens."""
+    K = 8 if dtype == "bf16" else 128
+    say("smallest", dtype, sf_fmt, gran)
+    p = synth.make_masked(dtype, 1, 1, 8, K, [1], seed=9, device=DEV, sf_fmt=sf_fmt,
+                          sfb_gran=gran)
+    for em in (0, 1, 200):
+        D = run_masked(p, em)
+        torch.cuda.synchronize()
+        assert_report(check_masked(p, D), dtype)
+    p = cut_contiguous_rows(synth.make_contiguous(dtype, 1, 8, K, [1], seed=10, device=DEV,
+                                                  sf_fmt=sf_fmt, sfb_gran=gran), 1)
+    D = run_contiguous(p, 1)
+    torch.cuda.synchronize()
+    assert_report(check_contiguous(p, D), dtype)
+    q = synth.make_contiguous_psum(dtype, 1, 8, K, [1], seed=11, device=DEV, sf_fmt=sf_fmt,
+                                   sfb_gran=gran)
+    assert q.M == 1
+    D = run_psum(q, 1)
+    torch.cuda.synchronize()
+    assert_report(check_psum(q, D), dtype)
+    if dtype == "fp8_fp4":
+        return  # FP4 weights are M-grouped only
+    ks = [8] if dtype == "bf16" else [128]
+    r = synth.make_kgrouped(dtype, ks, 1, 8, seed=12, device=DEV, std_a=1.0,
+                            zero_channel_k=-1, sf_fmt=sf_fmt)
+    D = run_kgrouped(r, accumulate=False)
+    torch.cuda.synchronize()
+    assert_report(check_kgrouped(r, D), dtype)
+
+
 def test_contiguous_matches_masked_bitwise():
     """The same expert rows through the masked and the contiguous entry points give
     identical bits (same engine, same K order)."""
