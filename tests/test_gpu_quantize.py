@@ -38,7 +38,7 @@ def draw(M, K, seed):
     x = torch.randn((M, K), device=DEV, generator=g)
     # row magnitudes over many binades, a few all-zero groups and a tiny-valued row
     x *= torch.exp2(torch.randint(-20, 12, (M, 1), device=DEV, generator=g).float())
-    x[3, 128:256] = 0
+    x[min(3, M - 1), 128:256] = 0
     x[min(7, M - 1)] *= 2.0 ** -110
     return x.to(torch.bfloat16)
 
@@ -49,6 +49,18 @@ def test_quantize_ragged_rows(fmt, z):
     X = draw(1000, 1024, 1)
     Q, SF = quantize(X, fmt, z)
     check(X, Q, SF, fmt, z)
+
+
+@pytest.mark.parametrize("K", [128, 256, 384, 640])
+def test_quantize_narrow_rows_few_rows(K):
+    """Rows of one to five 128-column groups (several rows share a wave) and 1 to 17 rows
+    (a partly filled last wave), both scale formats."""
+    for M in (1, 2, 3, 5, 17):
+        say("quantize narrow", M, K)
+        X = draw(M, K, 100 + M)
+        for fmt in ("f32", "ue8m0"):
+            Q, SF = quantize(X, fmt)
+            check(X, Q, SF, fmt)
 
 
 def test_quantize_midpoints_round_to_even():

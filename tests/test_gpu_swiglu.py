@@ -73,6 +73,17 @@ def test_swiglu_ragged_rows(fmt, z):
     check(H, Q, SF, fmt, z)
 
 
+@pytest.mark.parametrize("I", [128, 256, 384])
+def test_swiglu_narrow_rows_few_rows(I):
+    """One to three 128-column output groups per row and 1 to 17 rows, both formats."""
+    for M in (1, 2, 3, 5, 17):
+        say("swiglu narrow", M, I)
+        H = draw_h(M, I, 200 + M)
+        for fmt in ("f32", "ue8m0"):
+            Q, SF = swiglu_quant(H, fmt)
+            check(H, Q, SF, fmt)
+
+
 def test_swiglu_every_bf16_gate():
     """Every finite bf16 gate value with |g| < 2^9 (the exponent range where e^-g goes
     from 1 through subnormal to overflow), up = 1 or -3, in groups of 128."""
