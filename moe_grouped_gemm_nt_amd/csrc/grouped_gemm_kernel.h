@@ -662,9 +662,11 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
     dma_fence();
 #pragma unroll
     for (int u = 0; u < Lay::U_AB; ++u) {
-      // FP4 weight rows advance 64 bytes per slice (K is a multiple of 128: no tail)
+      // FP4 weight rows advance 64 bytes per slice. Only BF16 rows can end inside a
+      // slice: FP8 activations come in whole 128-K groups (an FP8 tile with no K, an empty
+      // K-grouped expert, has resources of size 0, so its copies read zeros anyway).
       uint32_t voff = I.vab[u] + (Lay::FP4W && u >= Lay::U_A ? s * Lay::B_ROW : kb0);
-      if (!Lay::FP4W && !full && kb0 + c16 + 16 > t.k_bytes) voff = kOOB;
+      if (!Lay::FP8 && !full && kb0 + c16 + 16 > t.k_bytes) voff = kOOB;
       // Weight rows read once stream past the caches (tiles built for it, chosen on the
       // host).
       if (u >= Lay::U_A && T::STREAMW)
