@@ -319,6 +319,19 @@ __device__ __forceinline__ void dma_x4_nt(uint32_t lds, v4i rsrc, uint32_t voff)
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
                :: "s"(l), "v"(voff), "s"(rsrc) : "memory");
 }
+// The same copies with a wave-uniform byte offset `soff` added to every lane's address (the
+// instruction's scalar offset operand): lanes whose voff is out of range stay out of range.
+__device__ __forceinline__ void dma_x4_so(uint32_t lds, v4i rsrc, uint32_t voff, uint32_t soff) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(l), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+__device__ __forceinline__ void dma_x4_nt_so(uint32_t lds, v4i rsrc, uint32_t voff,
+                                             uint32_t soff) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+               :: "s"(l), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
 __device__ __forceinline__ void dma_x1(uint32_t lds, v4i rsrc, uint32_t voff) {
   const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"

@@ -662,17 +662,30 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
     dma_fence();
 #pragma unroll
     for (int u = 0; u < Lay::U_AB; ++u) {
-      // FP4 weight rows advance 64 bytes per slice. Only BF16 rows can end inside a
-      // slice: FP8 activations come in whole 128-K groups (an FP8 tile with no K, an empty
-      // K-grouped expert, has resources of size 0, so its copies read zeros anyway).
-      uint32_t voff = I.vab[u] + (Lay::FP4W && u >= Lay::U_A ? s * Lay::B_ROW : kb0);
-      if (!Lay::FP8 && !full && kb0 + c16 + 16 > t.k_bytes) voff = kOOB;
-      // Weight rows read once stream past the caches (tiles built for it, chosen on the
-      // host).
-      if (u >= Lay::U_A && T::STREAMW)
-        dma_x4_nt(st + Lay::A_OFF + 1024 * (4 * u + cwave), I.rs_b, voff);
-      else
-        dma_x4(st + Lay::A_OFF + 1024 * (4 * u + cwave), u < Lay::U_A ? I.rs_a : I.rs_b, voff);
+      const uint32_t lds_u = st + Lay::A_OFF + 1024 * (4 * u + cwave);
+      if constexpr (Lay::FP8) {
+        // FP8 activations come in whole 128-K groups, so no row ends inside a slice (an
+        // FP8 tile with no K, an empty K-grouped expert, has resources of size 0 and its
+        // copies read zeros). The slice's K offset rides in the instruction's scalar
+        // offset, so a lane's offset (kOOB for rows outside the tile) is the same for every
+        // slice of the tile; FP4 weight rows advance 64 bytes per slice.
+        const uint32_t so = Lay::FP4W && u >= Lay::U_A ? (uint32_t)(s * Lay::B_ROW)
+                                                        : (uint32_t)kb0;
+        // Weight rows read once stream past the caches (tiles built for it, chosen on
+        // the host).
+        if (u >= Lay::U_A && T::STREAMW)
+          dma_x4_nt_so(lds_u, I.rs_b, I.vab[u], so);
+        else
+          dma_x4_so(lds_u, u < Lay::U_A ? I.rs_a : I.rs_b, I.vab[u], so);
+      } else {
+        // BF16 rows can end inside a slice: lanes past the row end read zeros
+        uint32_t voff = I.vab[u] + kb0;
+        if (!full && kb0 + c16 + 16 > t.k_bytes) voff = kOOB;
+        if (u >= Lay::U_A && T::STREAMW)
+          dma_x4_nt(lds_u, I.rs_b, voff);
+        else
+          dma_x4(lds_u, u < Lay::U_A ? I.rs_a : I.rs_b, voff);
+      }
     }
 #pragma unroll
     for (int us = 0; us < Lay::U_SM; ++us) {
