@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mgg {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -337,6 +339,15 @@ __device__ __forceinline__ void dma_x1(uint32_t lds, v4i rsrc, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :: "s"(l), "v"(voff), "s"(rsrc) : "memory");
 }
+// Calls f(std::integral_constant<int, I>) for I = B .. E - 1 in order.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // Pins a uniform value in SGPRs at this point of the program.
 __device__ __forceinline__ void pin_sgpr(v4i& r) { asm volatile("" : "+s"(r)); }
 

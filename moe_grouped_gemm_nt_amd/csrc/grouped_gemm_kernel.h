@@ -25,6 +25,8 @@
 // that publishes the last exchange tile), so nothing else needs synchronising.
 #pragma once
 
+#include <type_traits>
+
 #include "act_math.h"
 #include "gemm_engine.h"
 #include "tile_map.h"
@@ -94,20 +96,25 @@ struct Layout {
   // 8(4u + w) + 7 of the [A; B] tile, so A and B slots are fixed per u (BM % 32 == 0);
   // FP4 weight rows are 64 bytes, so a weight slot covers 16 of them.
   // Scale and row-index copies are few: they are dealt to the four waves ("small"
-  // slots, padded with a dummy copy).
+  // slots: small copy e goes to wave e % 4, so a wave issues U_SM or U_SM - 1 of them).
   static constexpr int U_A = T::BM / 32, U_B = T::BN * B_ROW / 4096, U_AB = U_A + U_B;
   static constexpr int SMALL = SA_INSTR + SB_INSTR + RI_INSTR;
   static constexpr int U_SM = cdiv(SMALL, 4);
-  static constexpr int PER_WAVE = U_AB + U_SM;  // copy instructions per wave per item
-  static constexpr bool HAS_DUMMY = U_SM * 4 > SMALL;
+  static constexpr int PER_WAVE = U_AB + U_SM;  // most copy instructions per wave per item
+  // copy instructions per item of copy wave cw: its operand slots and the small copies
+  // dealt to it (e = 4 us + cw < SMALL)
+  static constexpr int per_wave(int cw) {
+    int n = U_AB;
+    for (int us = 0; us < U_SM; ++us) n += 4 * us + cw < SMALL ? 1 : 0;
+    return n;
+  }
 
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = T::BM * kSliceBytes;
   static constexpr int SA_OFF = B_OFF + T::BN * B_ROW;
   static constexpr int SB_OFF = SA_OFF + SA_INSTR * 256;
   static constexpr int RI_OFF = SB_OFF + SB_INSTR * 256;
-  static constexpr int DUMMY_OFF = RI_OFF + RI_INSTR * 256;
-  static constexpr int STAGE = DUMMY_OFF + (HAS_DUMMY ? 256 : 0);
+  static constexpr int STAGE = RI_OFF + RI_INSTR * 256;
   static constexpr int PIPE = T::S * STAGE;
 
   // Accumulation: threads per workgroup (MFMA waves + epilogue waves) and the two fp32
@@ -651,9 +658,11 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
     }
   };
 
-  // ---- copies of one item (tile I.t, slice s) into stage `stg`; an idle cursor copies
-  // zeros so the instruction count never changes.
-  auto issue = [&](const Issue& I, int s, int stg) {
+  // ---- copies of one item (tile I.t, slice s) into stage `stg` by copy wave `cw` (a
+  // compile-time constant); an idle cursor copies zeros so a wave's instruction count per
+  // item never changes.
+  auto issue = [&](const Issue& I, int s, int stg, auto cw) {
+    constexpr int CW = decltype(cw)::value;
     const TileCtx& t = I.t;
     const uint32_t st = lds0 + stg * Lay::STAGE;
     const int kb0 = s * kSliceBytes;
@@ -662,7 +671,7 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
     dma_fence();
 #pragma unroll
     for (int u = 0; u < Lay::U_AB; ++u) {
-      const uint32_t lds_u = st + Lay::A_OFF + 1024 * (4 * u + cwave);
+      const uint32_t lds_u = st + Lay::A_OFF + 1024 * (4 * u + CW);
       if constexpr (Lay::FP8) {
         // FP8 activations come in whole 128-K groups, so no row ends inside a slice (an
         // FP8 tile with no K, an empty K-grouped expert, has resources of size 0 and its
@@ -687,10 +696,9 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
           dma_x4(lds_u, u < Lay::U_A ? I.rs_a : I.rs_b, voff);
       }
     }
-#pragma unroll
-    for (int us = 0; us < Lay::U_SM; ++us) {
-      const int e = 4 * us + cwave;  // small-copy index dealt to this wave (uniform)
-      if (e < Lay::SA_INSTR) {
+    static_for<0, Lay::U_SM>([&](auto us_c) {
+      constexpr int e = 4 * decltype(us_c)::value + CW;  // small copy dealt to this wave
+      if constexpr (e < Lay::SA_INSTR) {
         const int l = 64 * e + lane;
         const long o = t.sfa_off + (long)s * t.sfa_ld + t.m0;
         uint32_t voff = kOOB;
@@ -700,7 +708,7 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
           if (t.valid && k_any && l < Lay::SA_LANES) voff = (uint32_t)((o & ~3L) + 4 * l);
         }
         dma_x1(st + Lay::SA_OFF + 256 * e, rs_sfa, voff);
-      } else if (e < Lay::SA_INSTR + Lay::SB_INSTR) {
+      } else if constexpr (e < Lay::SA_INSTR + Lay::SB_INSTR) {
         const int j = e - Lay::SA_INSTR;
         const int l = 64 * j + lane;
         uint32_t voff = kOOB;
@@ -722,16 +730,14 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
             voff = SF == kSfF32 ? (uint32_t)(o * 4) : (uint32_t)(o & ~3L);
         }
         dma_x1(st + Lay::SB_OFF + 256 * j, rs_sfb, voff);
-      } else if (e < Lay::SMALL) {
+      } else if constexpr (e < Lay::SMALL) {
         const int j = e - Lay::SA_INSTR - Lay::SB_INSTR;
         const int l = 64 * j + lane;
         const int m = t.m0 + l;
         dma_x1(st + Lay::RI_OFF + 256 * j, rs_meta,
                (t.valid && l < T::BM && m < p.rows) ? (uint32_t)(m * 4) : kOOB);
-      } else {
-        dma_x1(st + Lay::DUMMY_OFF, rs_meta, kOOB);  // keeps the per-wave count uniform
       }
-    }
+    });
   };
 
   // ---- per-lane constant LDS offsets of the MFMA fragments (XOR swizzle folded in)
@@ -1164,29 +1170,40 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
   }
   if (wave >= Lay::COPY0) {
     // Copy waves (the last four): one barrier per item, like the MFMA waves. Before
-    // barrier j the copies of item j have landed (the PER_WAVE * (S - 2) younger ones
-    // may still be in flight); after it the stage of item j + S - 1 is free and is
-    // refilled. The MFMA waves therefore never wait to enter the memory pipeline.
-    prepare(ic);
+    // barrier j the copies of item j have landed (the younger ones, per_wave(CW) per item
+    // for S - 2 items, may still be in flight); after it the stage of item j + S - 1 is
+    // free and is refilled. The MFMA waves therefore never wait to enter the memory
+    // pipeline. The loop is instantiated per copy wave, so the small copies dealt to a
+    // wave and its wait counts are compile-time constants.
+    auto copy_loop = [&](auto cw) {
+      constexpr int CW = decltype(cw)::value;
+      prepare(ic);
 #pragma unroll
-    for (int k = 0; k < S - 1; ++k) {
-      issue(ic, si, k);
-      if (advance(ic.t, Li, si)) prepare(ic);
+      for (int k = 0; k < S - 1; ++k) {
+        issue(ic, si, k, cw);
+        if (advance(ic.t, Li, si)) prepare(ic);
+      }
+      TileCtx tm = tc;  // mirror of the compute cursor: the same number of barriers
+      long Lm = Lc;
+      int sm = 0, jt = 0;
+      while (true) {
+        vm_wait_imm<Lay::per_wave(CW) * (S - 2)>();
+        lds_barrier();
+        issue(ic, si, (jt + S - 1) % S, cw);
+        if (advance(ic.t, Li, si)) prepare(ic);
+        advance(tm, Lm, sm);
+        if (!tm.valid) break;
+        ++jt;
+      }
+      if constexpr (ACC) lds_barrier();  // the MFMA waves' final exchange barrier
+      vm_wait_imm<0>();  // the last (idle) copies land before the workgroup's LDS is released
+    };
+    switch (cwave) {
+      case 0: copy_loop(std::integral_constant<int, 0>{}); break;
+      case 1: copy_loop(std::integral_constant<int, 1>{}); break;
+      case 2: copy_loop(std::integral_constant<int, 2>{}); break;
+      default: copy_loop(std::integral_constant<int, 3>{}); break;
     }
-    TileCtx tm = tc;  // mirror of the compute cursor: the same number of barriers
-    long Lm = Lc;
-    int sm = 0, jt = 0;
-    while (true) {
-      vm_wait_imm<Lay::PER_WAVE * (S - 2)>();
-      lds_barrier();
-      issue(ic, si, (jt + S - 1) % S);
-      if (advance(ic.t, Li, si)) prepare(ic);
-      advance(tm, Lm, sm);
-      if (!tm.valid) break;
-      ++jt;
-    }
-    if constexpr (ACC) lds_barrier();  // the MFMA waves' final exchange barrier
-    vm_wait_imm<0>();  // the last (idle) copies land before the workgroup's LDS is released
     return;
   }
   // MFMA waves

@@ -332,10 +332,10 @@ def test_fused_swiglu_full_w13_shape():
 
 # Row blocks at which the three-stage fused tile's scheduler table (4 bytes per 128-row
 # block, after three 50 176 .. 51 200-byte pipeline stages) still fits in 160 KB of LDS:
-# float32 scales with 128 x 128 weight blocks 2944, with per-channel weight scales 2560.
+# float32 scales with 128 x 128 weight blocks 3136, with per-channel weight scales 2560.
 # One block more and the host falls back to the two-stage tile; 4096 blocks (524288 rows)
 # is the contiguous layout's maximum.
-@pytest.mark.parametrize("gran,blocks", [("block128", 2944), ("block128", 2945),
+@pytest.mark.parametrize("gran,blocks", [("block128", 3136), ("block128", 3137),
                                          ("channel", 2560), ("channel", 2561),
                                          ("block128", 4096)])
 def test_fused_swiglu_row_block_limits(gran, blocks):
