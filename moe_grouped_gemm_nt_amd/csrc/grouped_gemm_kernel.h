@@ -669,32 +669,38 @@ __global__ __launch_bounds__((Layout<T, VAR, DT, SF, GRAN, ACC>::NT)) void group
     const bool full = kb0 + kSliceBytes <= t.k_bytes;  // no K tail inside this slice
     const bool k_any = t.k_bytes > 0;
     dma_fence();
+    // Rows that end inside the slice (a BF16 K tail) need a per-lane test; every other
+    // slice copies with the slice's K offset in the instruction's scalar offset, so a
+    // lane's offset (kOOB for rows outside the tile) is the same for every slice of the
+    // tile. FP8 activations come in whole 128-K groups, so FP8 slices are never cut (an
+    // FP8 tile with no K, an empty K-grouped expert, has resources of size 0 and its
+    // copies read zeros); FP4 weight rows advance 64 bytes per slice.
+    auto operands = [&](auto tail) {
 #pragma unroll
-    for (int u = 0; u < Lay::U_AB; ++u) {
-      const uint32_t lds_u = st + Lay::A_OFF + 1024 * (4 * u + CW);
-      if constexpr (Lay::FP8) {
-        // FP8 activations come in whole 128-K groups, so no row ends inside a slice (an
-        // FP8 tile with no K, an empty K-grouped expert, has resources of size 0 and its
-        // copies read zeros). The slice's K offset rides in the instruction's scalar
-        // offset, so a lane's offset (kOOB for rows outside the tile) is the same for every
-        // slice of the tile; FP4 weight rows advance 64 bytes per slice.
-        const uint32_t so = Lay::FP4W && u >= Lay::U_A ? (uint32_t)(s * Lay::B_ROW)
-                                                        : (uint32_t)kb0;
+      for (int u = 0; u < Lay::U_AB; ++u) {
+        const uint32_t lds_u = st + Lay::A_OFF + 1024 * (4 * u + CW);
+        const v4i rs = u < Lay::U_A ? I.rs_a : I.rs_b;
         // Weight rows read once stream past the caches (tiles built for it, chosen on
         // the host).
-        if (u >= Lay::U_A && T::STREAMW)
-          dma_x4_nt_so(lds_u, I.rs_b, I.vab[u], so);
-        else
-          dma_x4_so(lds_u, u < Lay::U_A ? I.rs_a : I.rs_b, I.vab[u], so);
-      } else {
-        // BF16 rows can end inside a slice: lanes past the row end read zeros
-        uint32_t voff = I.vab[u] + kb0;
-        if (!full && kb0 + c16 + 16 > t.k_bytes) voff = kOOB;
-        if (u >= Lay::U_A && T::STREAMW)
-          dma_x4_nt(lds_u, I.rs_b, voff);
-        else
-          dma_x4(lds_u, u < Lay::U_A ? I.rs_a : I.rs_b, voff);
+        constexpr bool nt_w = T::STREAMW;
+        if constexpr (decltype(tail)::value) {
+          uint32_t voff = I.vab[u] + kb0;
+          if (kb0 + c16 + 16 > t.k_bytes) voff = kOOB;
+          if (u >= Lay::U_A && nt_w) dma_x4_nt(lds_u, rs, voff);
+          else dma_x4(lds_u, rs, voff);
+        } else {
+          const uint32_t so = Lay::FP4W && u >= Lay::U_A ? (uint32_t)(s * Lay::B_ROW)
+                                                          : (uint32_t)kb0;
+          if (u >= Lay::U_A && nt_w) dma_x4_nt_so(lds_u, rs, I.vab[u], so);
+          else dma_x4_so(lds_u, rs, I.vab[u], so);
+        }
       }
+    };
+    if constexpr (Lay::FP8) {
+      operands(std::false_type{});
+    } else {
+      if (full) operands(std::false_type{});
+      else operands(std::true_type{});
     }
     static_for<0, Lay::U_SM>([&](auto us_c) {
       constexpr int e = 4 * decltype(us_c)::value + CW;  // small copy dealt to this wave
